@@ -1,0 +1,380 @@
+// Engine: workspace, metadata staging and the launch sequence of one
+// heterogeneous-batch step (forward + emit of the unified runner,
+// Efficient Iterative Retrieval with Heterogeneous Batching §3.1).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "orthrus_internal.h"
+
+using namespace orthrus;
+
+struct orthrus_engine {
+  orthrus_model_cfg cfg{};
+  orthrus_weights w{};
+  std::vector<orthrus_layer_w> layers;
+  uint16_t *kc = nullptr, *vc = nullptr;
+  int device = 0;
+  // workspace
+  float *x = nullptr;
+  uint16_t *h = nullptr, *qkv = nullptr, *o = nullptr, *act = nullptr, *U = nullptr;
+  float *hf = nullptr;
+  uint16_t *hl = nullptr;
+  double *inv_freq = nullptr;
+  float *part_ml = nullptr, *part_o = nullptr;
+  size_t part_cap = 0;  // in split units
+  int32_t *meta_dev = nullptr;
+  int32_t *meta_host = nullptr;
+  size_t meta_cap = 0;  // int32 words
+  hipEvent_t staged{};
+  bool staged_pending = false;
+  std::string err;
+  // scratch host vectors
+  HostPack pack;
+  std::vector<AttnWork> work;
+  std::vector<DevItem> items;
+};
+
+namespace {
+
+orthrus_status hip_fail(orthrus_engine *e, hipError_t r, const char *what) {
+  if (e) e->err = std::string(what) + ": " + hipGetErrorString(r);
+  return ORTHRUS_EHIP;
+}
+
+#define HIPCHK(call, what)                               \
+  do {                                                   \
+    hipError_t r_ = (call);                              \
+    if (r_ != hipSuccess) return hip_fail(eng, r_, what); \
+  } while (0)
+
+#define LCHK(call, what)                                               \
+  do {                                                                 \
+    int r_ = (call);                                                   \
+    if (r_ != 0) return hip_fail(eng, (hipError_t)r_, what);           \
+  } while (0)
+
+size_t align4(size_t n) { return (n + 3) & ~(size_t)3; }
+
+}  // namespace
+
+namespace orthrus {
+
+void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const HostPack &p,
+                     std::vector<AttnWork> &work, std::vector<DevItem> &items, int &n_parts) {
+  const int G = cfg.n_q_heads / cfg.n_kv_heads;
+  const int QB = ATTN_ROWS / G;
+  work.clear();
+  items.assign(b.n_items, DevItem{});
+  std::vector<AttnWork> dec;
+  n_parts = 0;
+  for (int i = 0; i < b.n_items; ++i) {
+    const orthrus_item &it = b.items[i];
+    DevItem &d = items[i];
+    d.row0 = p.cu_q[i];
+    d.n = it.n_tokens;
+    d.ctx = it.ctx_len;
+    d.page_off = it.page_off;
+    d.kind = it.kind;
+    if (it.kind != ORTHRUS_DECODE) {
+      for (int g = 0; g < cfg.n_kv_heads; ++g)
+        for (int q0 = 0; q0 < it.n_tokens; q0 += QB) {
+          const int qn = std::min(QB, it.n_tokens - q0);
+          work.push_back({WORK_CHUNK, i, g, q0, qn, 0, it.ctx_len + q0 + qn, 0});
+        }
+    } else {
+      const int nk = it.ctx_len + 1;
+      const int ns = (nk + ATTN_SPLIT - 1) / ATTN_SPLIT;
+      d.part0 = n_parts;
+      d.n_parts = ns;
+      for (int g = 0; g < cfg.n_kv_heads; ++g)
+        for (int s = 0; s < ns; ++s) {
+          const int k0 = s * ATTN_SPLIT;
+          dec.push_back({WORK_DECODE, i, g, 0, 1, k0, std::min(nk, k0 + ATTN_SPLIT), n_parts + g * ns + s});
+        }
+      n_parts += cfg.n_kv_heads * ns;
+    }
+  }
+  // heaviest first: chunk tiles by (rows x keys), then decode splits
+  std::stable_sort(work.begin(), work.end(), [](const AttnWork &a, const AttnWork &c) {
+    return (long)a.qn * a.k1 > (long)c.qn * c.k1;
+  });
+  work.insert(work.end(), dec.begin(), dec.end());
+}
+
+}  // namespace orthrus
+
+extern "C" {
+
+const char *orthrus_last_error(const orthrus_engine *eng) { return eng ? eng->err.c_str() : ""; }
+
+static void free_all(orthrus_engine *e) {
+  void *ptrs[] = {e->x, e->h, e->qkv, e->o, e->act, e->U, e->hf, e->hl, e->inv_freq,
+                  e->part_ml, e->part_o, e->meta_dev};
+  for (void *p : ptrs)
+    if (p) (void)hipFree(p);
+  if (e->meta_host) (void)hipHostFree(e->meta_host);
+  if (e->staged) (void)hipEventDestroy(e->staged);
+}
+
+orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weights *w, void *k_pages,
+                              void *v_pages, orthrus_engine **out) {
+  if (!cfg || !w || !out || !k_pages || !v_pages || !w->layers) return ORTHRUS_EINVAL;
+  *out = nullptr;
+  const orthrus_model_cfg &c = *cfg;
+  const int hd = c.head_dim;
+  if (c.n_layers < 1 || c.d_model < 8 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.vocab < 1 ||
+      c.ffn_dim < 8 || c.page_size < 1 || c.n_pages < 1 || c.max_tokens < 1 || c.max_items < 1 ||
+      c.max_pool_slots < 0 || c.lora_rank < 0)
+    return ORTHRUS_EINVAL;
+  if (!(hd == 16 || hd == 32 || hd == 64 || hd == 128)) return ORTHRUS_EINVAL;
+  if (c.n_q_heads % c.n_kv_heads) return ORTHRUS_EINVAL;
+  const int G = c.n_q_heads / c.n_kv_heads;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return ORTHRUS_EINVAL;
+  if (c.d_model % 8 || c.ffn_dim % 8 || c.lora_rank % 8) return ORTHRUS_EINVAL;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const orthrus_layer_w &L = w->layers[l];
+    if (!L.w_qkv || !L.w_o || !L.w_gate_up || !L.w_down || !L.g_attn || !L.g_ffn) return ORTHRUS_EINVAL;
+    if (c.lora_rank > 0 && (!L.lora_a_qkv || !L.lora_b_qkv || !L.lora_a_o || !L.lora_b_o))
+      return ORTHRUS_EINVAL;
+  }
+  if (!w->tok_emb || !w->lm_head || !w->g_final) return ORTHRUS_EINVAL;
+
+  orthrus_engine *eng = new orthrus_engine();
+  eng->cfg = c;
+  eng->w = *w;
+  eng->layers.assign(w->layers, w->layers + c.n_layers);
+  eng->w.layers = eng->layers.data();
+  eng->kc = (uint16_t *)k_pages;
+  eng->vc = (uint16_t *)v_pages;
+  auto bail = [&](orthrus_status s) {
+    free_all(eng);
+    delete eng;
+    return s;
+  };
+  if (hipGetDevice(&eng->device) != hipSuccess) return bail(ORTHRUS_EHIP);
+  const size_t T = c.max_tokens, d = c.d_model;
+  const size_t qkvd = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * hd, qd = (size_t)c.n_q_heads * hd;
+  struct {
+    void **p;
+    size_t bytes;
+  } allocs[] = {
+      {(void **)&eng->x, T * d * 4},
+      {(void **)&eng->h, T * std::max(d, qd) * 2},
+      {(void **)&eng->qkv, T * qkvd * 2},
+      {(void **)&eng->o, T * qd * 2},
+      {(void **)&eng->act, T * (size_t)c.ffn_dim * 2},
+      {(void **)&eng->U, T * (size_t)std::max(3 * c.lora_rank, 8) * 2},
+      {(void **)&eng->hf, T * d * 4},
+      {(void **)&eng->hl, T * d * 2},
+      {(void **)&eng->inv_freq, (size_t)hd / 2 * 8},
+  };
+  for (auto &a : allocs)
+    if (hipMalloc(a.p, a.bytes) != hipSuccess) return bail(ORTHRUS_ENOMEM);
+  std::vector<double> inv(hd / 2);
+  for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / hd);
+  if (hipMemcpy(eng->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice) != hipSuccess)
+    return bail(ORTHRUS_EHIP);
+  if (hipEventCreateWithFlags(&eng->staged, hipEventDisableTiming) != hipSuccess) return bail(ORTHRUS_EHIP);
+  *out = eng;
+  return ORTHRUS_OK;
+}
+
+void orthrus_destroy(orthrus_engine *eng) {
+  if (!eng) return;
+  (void)hipSetDevice(eng->device);
+  (void)hipDeviceSynchronize();
+  free_all(eng);
+  delete eng;
+}
+
+orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, const orthrus_pool_state *pool,
+                            float *logits, int32_t logits_cap_rows, float *emb, int32_t emb_cap_rows,
+                            int32_t *n_logits, int32_t *n_emb, float *hidden_out, void *stream) {
+  if (!eng) return ORTHRUS_EINVAL;
+  eng->err.clear();
+  if (!batch || !pool) {
+    eng->err = "null batch or pool state";
+    return ORTHRUS_EINVAL;
+  }
+  const orthrus_model_cfg &c = eng->cfg;
+  char msg[256];
+  HostPack &p = eng->pack;
+  orthrus_status st = validate_and_pack(c, *batch, p, msg, sizeof msg);
+  if (st != ORTHRUS_OK) {
+    eng->err = msg;
+    return st;
+  }
+  const int G = (int)p.logit_rows.size();
+  if (G > logits_cap_rows || p.n_emb > emb_cap_rows) {
+    eng->err = "output capacity too small";
+    return ORTHRUS_ECAPACITY;
+  }
+  if ((G > 0 && !logits) || (p.n_emb > 0 && !emb) ||
+      (p.rows_by_kind[0] > 0 && (!pool->sum || !pool->wsum || !pool->kept))) {
+    eng->err = "null output or pool buffer";
+    return ORTHRUS_EINVAL;
+  }
+  if (n_logits) *n_logits = G;
+  if (n_emb) *n_emb = p.n_emb;
+  const int T = p.n_tokens;
+  if (T == 0) return ORTHRUS_OK;
+
+  int n_parts = 0;
+  build_attn_work(c, *batch, p, eng->work, eng->items, n_parts);
+  std::vector<int32_t> dec_items;
+  for (int i = 0; i < batch->n_items; ++i)
+    if (batch->items[i].kind == ORTHRUS_DECODE) dec_items.push_back(i);
+
+  HIPCHK(hipSetDevice(eng->device), "hipSetDevice");
+  hipStream_t s = (hipStream_t)stream;
+
+  // metadata block (int32 words, 16-byte aligned sections)
+  const size_t n_segs = p.pool_segs.size() / 8;
+  size_t off = 0;
+  const size_t o_tok = off; off = align4(off + T);
+  const size_t o_pos = off; off = align4(off + T);
+  const size_t o_slot = off; off = align4(off + T);
+  const size_t o_pages = off; off = align4(off + (size_t)batch->n_page_ids);
+  const size_t o_logit = off; off = align4(off + G);
+  const size_t o_segs = off; off = align4(off + n_segs * 8);
+  const size_t o_dec = off; off = align4(off + dec_items.size());
+  const size_t o_items = off; off = align4(off + eng->items.size() * 8);
+  const size_t o_work = off; off = align4(off + eng->work.size() * 8);
+  const size_t words = std::max<size_t>(off, 4);
+  if (eng->staged_pending) {
+    HIPCHK(hipEventSynchronize(eng->staged), "hipEventSynchronize");
+    eng->staged_pending = false;
+  }
+  if (words > eng->meta_cap) {
+    const size_t cap = words * 2;
+    if (eng->meta_dev) {
+      HIPCHK(hipDeviceSynchronize(), "hipDeviceSynchronize");
+      (void)hipFree(eng->meta_dev);
+      (void)hipHostFree(eng->meta_host);
+      eng->meta_dev = nullptr;
+      eng->meta_host = nullptr;
+      eng->meta_cap = 0;
+    }
+    if (hipMalloc(&eng->meta_dev, cap * 4) != hipSuccess ||
+        hipHostMalloc(&eng->meta_host, cap * 4, hipHostMallocDefault) != hipSuccess) {
+      eng->err = "metadata allocation failed";
+      return ORTHRUS_ENOMEM;
+    }
+    eng->meta_cap = cap;
+  }
+  if ((size_t)n_parts > eng->part_cap) {
+    const size_t cap = (size_t)n_parts * 2;
+    HIPCHK(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    if (eng->part_ml) (void)hipFree(eng->part_ml);
+    if (eng->part_o) (void)hipFree(eng->part_o);
+    eng->part_ml = eng->part_o = nullptr;
+    eng->part_cap = 0;
+    const int Gq = c.n_q_heads / c.n_kv_heads;
+    if (hipMalloc(&eng->part_ml, cap * ATTN_WAVES * Gq * 2 * 4) != hipSuccess ||
+        hipMalloc(&eng->part_o, cap * ATTN_WAVES * Gq * (size_t)c.head_dim * 4) != hipSuccess) {
+      eng->err = "partial buffer allocation failed";
+      return ORTHRUS_ENOMEM;
+    }
+    eng->part_cap = cap;
+  }
+  int32_t *mh = eng->meta_host;
+  memcpy(mh + o_tok, batch->token_ids, (size_t)T * 4);
+  memcpy(mh + o_pos, p.pos.data(), (size_t)T * 4);
+  memcpy(mh + o_slot, p.slot.data(), (size_t)T * 4);
+  if (batch->n_page_ids) memcpy(mh + o_pages, batch->page_ids, (size_t)batch->n_page_ids * 4);
+  if (G) memcpy(mh + o_logit, p.logit_rows.data(), (size_t)G * 4);
+  if (n_segs) memcpy(mh + o_segs, p.pool_segs.data(), n_segs * 8 * 4);
+  if (!dec_items.empty()) memcpy(mh + o_dec, dec_items.data(), dec_items.size() * 4);
+  if (!eng->items.empty()) memcpy(mh + o_items, eng->items.data(), eng->items.size() * 32);
+  if (!eng->work.empty()) memcpy(mh + o_work, eng->work.data(), eng->work.size() * 32);
+  HIPCHK(hipMemcpyAsync(eng->meta_dev, mh, words * 4, hipMemcpyHostToDevice, s), "metadata upload");
+  HIPCHK(hipEventRecord(eng->staged, s), "hipEventRecord");
+  eng->staged_pending = true;
+
+  const int32_t *d_tok = eng->meta_dev + o_tok, *d_pos = eng->meta_dev + o_pos;
+  const int32_t *d_slot = eng->meta_dev + o_slot, *d_pages = eng->meta_dev + o_pages;
+  const int32_t *d_logit = eng->meta_dev + o_logit, *d_segs = eng->meta_dev + o_segs;
+  const int32_t *d_dec = eng->meta_dev + o_dec;
+  const DevItem *d_items = (const DevItem *)(eng->meta_dev + o_items);
+  const AttnWork *d_work = (const AttnWork *)(eng->meta_dev + o_work);
+
+  const int d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, F = c.ffn_dim;
+  const int qd = Hq * hd, kvd = Hkv * hd, qkvd = qd + 2 * kvd, r = c.lora_rank;
+  const int TE = p.rows_by_kind[0];
+  const size_t layer_kv = (size_t)c.n_pages * Hkv * c.page_size * hd;
+
+  LCHK(launch_embed_gather(d_tok, (const uint16_t *)eng->w.tok_emb, eng->x, T, d, s), "embed_gather");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const orthrus_layer_w &L = eng->layers[l];
+    uint16_t *kc = eng->kc + (size_t)l * layer_kv, *vc = eng->vc + (size_t)l * layer_kv;
+    const bool lora = r > 0 && TE > 0;
+    LCHK(launch_rmsnorm(eng->x, (const uint16_t *)L.g_attn, eng->h, T, d, c.rms_eps, s), "rmsnorm");
+    LoraArgs la{};
+    if (lora) {
+      LCHK(launch_gemm(eng->h, d, (const uint16_t *)L.lora_a_qkv, d, eng->U, 3 * r, TE, 3 * r, d, EPI_BF16, 0,
+                       c.lora_scale, nullptr, s),
+           "lora_shrink_qkv");
+      la.U = eng->U; la.ldu = 3 * r; la.Bx = (const uint16_t *)L.lora_b_qkv; la.r = r; la.rows = TE;
+      la.sec1 = qd; la.sec2 = qd + kvd;
+    }
+    LCHK(launch_gemm(eng->h, d, (const uint16_t *)L.w_qkv, d, eng->qkv, qkvd, T, qkvd, d, EPI_BF16, 0, 1.f,
+                     lora ? &la : nullptr, s),
+         "gemm_qkv");
+    LCHK(launch_rope_kv(eng->qkv, d_pos, d_slot, eng->inv_freq, kc, vc, T, Hq, Hkv, hd, c.page_size, s),
+         "rope_kv");
+    LCHK(launch_attention(eng->qkv, qkvd, kc, vc, d_pages, d_items, d_work, (int)eng->work.size(),
+                          eng->part_ml, eng->part_o, eng->o, qd, Hq, Hkv, hd, c.page_size, s),
+         "attention");
+    LCHK(launch_attn_combine(d_items, d_dec, (int)dec_items.size(), eng->part_ml, eng->part_o, eng->o, qd,
+                             Hq, Hkv, hd, s),
+         "attn_combine");
+    if (lora) {
+      LCHK(launch_gemm(eng->o, qd, (const uint16_t *)L.lora_a_o, qd, eng->U, r, TE, r, qd, EPI_BF16, 0,
+                       c.lora_scale, nullptr, s),
+           "lora_shrink_o");
+      la.ldu = r; la.Bx = (const uint16_t *)L.lora_b_o; la.sec1 = d; la.sec2 = d;
+    }
+    LCHK(launch_gemm(eng->o, qd, (const uint16_t *)L.w_o, qd, eng->x, d, T, d, qd, EPI_RESID, 0, 1.f,
+                     lora ? &la : nullptr, s),
+         "gemm_o");
+    LCHK(launch_rmsnorm(eng->x, (const uint16_t *)L.g_ffn, eng->h, T, d, c.rms_eps, s), "rmsnorm");
+    LCHK(launch_gemm(eng->h, d, (const uint16_t *)L.w_gate_up, d, eng->act, F, T, F, d, EPI_SWIGLU, F, 1.f,
+                     nullptr, s),
+         "gemm_gate_up");
+    LCHK(launch_gemm(eng->act, F, (const uint16_t *)L.w_down, F, eng->x, d, T, d, F, EPI_RESID, 0, 1.f,
+                     nullptr, s),
+         "gemm_down");
+  }
+  if (hidden_out)
+    HIPCHK(hipMemcpyAsync(hidden_out, eng->x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s), "hidden copy");
+  LCHK(launch_final_norm(eng->x, (const uint16_t *)eng->w.g_final, d_logit, TE, G, eng->hf, eng->hl, d,
+                         c.rms_eps, s),
+       "final_norm");
+  if (G > 0)
+    LCHK(launch_gemm(eng->hl, d, (const uint16_t *)eng->w.lm_head, d, logits, c.vocab, G, c.vocab, d, EPI_F32,
+                     0, 1.f, nullptr, s),
+         "lm_head");
+  if (n_segs)
+    LCHK(launch_pool(eng->hf, d_segs, (int)n_segs, pool->sum, pool->wsum, pool->kept, emb, d, s), "pool");
+  return ORTHRUS_OK;
+}
+
+orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int32_t ldb, void *C, int32_t ldc,
+                                 int32_t M, int32_t N, int32_t K, int32_t epilogue, int32_t b_up_row,
+                                 void *stream) {
+  if (!A || !B || !C || M < 0 || N < 0 || K < 8 || K % 8 || lda % 8 || ldb % 8 || lda < K || ldb < K ||
+      epilogue < 0 || epilogue > 3 || ldc < N)
+    return ORTHRUS_EINVAL;
+  if (epilogue == EPI_SWIGLU && b_up_row < N) return ORTHRUS_EINVAL;
+  const int r = launch_gemm((const uint16_t *)A, lda, (const uint16_t *)B, ldb, C, ldc, M, N, K, epilogue,
+                            b_up_row, 1.f, nullptr, stream);
+  return r ? ORTHRUS_EHIP : ORTHRUS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,400 @@
+// Ragged causal attention over the paged KV cache, one launch for every
+// item type, plus the log-sum-exp combine of decode splits.
+//
+// Efficient Iterative Retrieval with Heterogeneous Batching: §3.2 Batch
+// Unit (embedding chunks, prefill chunks and decode rows share one pass and
+// differ only in length), §2.2 Generation (a decode step reads the cached
+// KV of all earlier tokens — memory-bound — while chunk rows are a dense,
+// compute-bound pass), §1 and §2.3 (chunks of one request are processed
+// across iterations; a later chunk attends to the KV its earlier chunks
+// left in the cache).  Row j of an item with context c sits at position
+// c + j and sees keys 0 .. c + j; query head h reads KV head h / (Hq/Hkv).
+//
+// Work entries (built on the host, heaviest first):
+//  CHUNK  : 128 (token, head) rows of one item and KV head.  Scores are
+//           formed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMAs with K
+//           staged in LDS; P^T stays in registers and O^T = V^T P^T reads a
+//           transposed V tile from LDS.  Online softmax in fp32 (exp2).
+//  DECODE : one decode row, one KV head, up to 256 keys; each wave walks
+//           64 keys with HD/8 lanes per key so every page (page_size x HD
+//           contiguous bf16) is read with 16-byte coalesced loads, serving
+//           all grouped query heads from one read; it writes (max, sum,
+//           unnormalised output) for the combine.
+#include "device_common.h"
+#include "orthrus_internal.h"
+
+namespace orthrus {
+
+struct AttnArgs {
+  const uint16_t *qkv;
+  const uint16_t *kc;
+  const uint16_t *vc;
+  const int32_t *page_ids;
+  const DevItem *items;
+  const AttnWork *work;
+  float *part_ml;
+  float *part_o;
+  uint16_t *o;
+  int ld_qkv, ld_o, Hq, Hkv, ps;
+  float scale_log2;
+};
+
+constexpr int KT = 64;  // keys per chunk-path tile
+
+template <int HD>
+struct ChunkSmem {
+  static constexpr int VTS = KT + 4;                // padded row of the transposed V tile
+  static constexpr int VROWS = HD < 32 ? 32 : HD;   // MFMA blocks are 32 rows of the head dim
+  uint16_t K[KT * HD];
+  uint16_t Vt[VROWS * VTS];
+};
+
+template <int HD>
+__device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &sm) {
+  constexpr int NCH = HD / 8;          // 16-byte chunks per key row
+  constexpr int VTS = ChunkSmem<HD>::VTS;
+  constexpr int NDB = HD < 32 ? 1 : HD / 32;  // 32-wide blocks of the head dim
+  const int G = a.Hq / a.Hkv;
+  const DevItem it = a.items[w.item];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5;
+  const int r = wave * 32 + (lane & 31);
+  const int tok = w.q0 + r / G;
+  const int head = w.kvh * G + r % G;
+  const bool rvalid = (r / G) < w.qn;
+  const int rpos = it.ctx + tok;
+  const int nkeys = it.ctx + w.q0 + w.qn;
+
+  bf16x8_t q[HD / 16];
+  {
+    const uint16_t *qrow = a.qkv + (size_t)(it.row0 + (rvalid ? tok : 0)) * a.ld_qkv + head * HD;
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (rvalid) v = *(const u32x4_t *)(qrow + kk * 16 + half * 8);
+      q[kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  f32x16_t oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int32_t *pages = a.page_ids + it.page_off;
+  const int min_rpos = it.ctx + w.q0;
+  if (HD < 32) {  // rows HD..31 of the transposed V tile stay zero
+    for (int c = tid; c < (32 - HD) * VTS; c += 256) sm.Vt[HD * VTS + c] = 0;
+  }
+
+  for (int kt0 = 0; kt0 < nkeys; kt0 += KT) {
+    __syncthreads();
+    // stage K (swizzled) and V (transposed) for keys kt0 .. kt0+KT-1
+    for (int c = tid; c < KT * NCH; c += 256) {
+      const int key = c / NCH, dc = c % NCH;
+      const int p = kt0 + key;
+      u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (p < nkeys) {
+        const int page = pages[p / a.ps];
+        const size_t off = (((size_t)page * a.Hkv + w.kvh) * a.ps + p % a.ps) * HD + dc * 8;
+        kv = *(const u32x4_t *)(a.kc + off);
+        vv = *(const u32x4_t *)(a.vc + off);
+      }
+      *(u32x4_t *)(&sm.K[key * HD + ((dc ^ (key & (NCH - 1))) * 8)]) = kv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm.Vt[(dc * 8 + 2 * e) * VTS + key] = (uint16_t)(vv[e] & 0xffffu);
+        sm.Vt[(dc * 8 + 2 * e + 1) * VTS + key] = (uint16_t)(vv[e] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // S^T for two 32-key blocks
+    f32x16_t s[KT / 32];
+#pragma unroll
+    for (int kb = 0; kb < KT / 32; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+      const int key = kb * 32 + (lane & 31);
+#pragma unroll
+      for (int kk = 0; kk < HD / 16; ++kk) {
+        const int ch = kk * 2 + half;
+        const bf16x8_t kop = __builtin_bit_cast(
+            bf16x8_t, *(const u32x4_t *)(&sm.K[key * HD + ((ch ^ (key & (NCH - 1))) * 8)]));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[kk], s[kb], 0, 0, 0);
+      }
+    }
+    // mask, scale, tile max
+    const bool need_mask = (kt0 + KT - 1) > min_rpos || !rvalid;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KT / 32; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kt0 + kb * 32 + (e / 4) * 8 + half * 4 + (e % 4);
+        float v = s[kb][e] * a.scale_log2;
+        if (need_mask && (!rvalid || key > rpos)) v = -INFINITY;
+        s[kb][e] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    m_run = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KT / 32; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2f(s[kb][e] - m_use);
+        s[kb][e] = p;
+        lsum += p;
+      }
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+
+    // O^T += V^T P^T in 16-key steps
+#pragma unroll
+    for (int st = 0; st < KT / 16; ++st) {
+      const int kb = st / 2, e0 = (st % 2) * 8;
+      u32x4_t pw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[i] = pack_bf2(s[kb][e0 + 2 * i], s[kb][e0 + 2 * i + 1]);
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw);
+      const int kbase = st * 16 + half * 4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int dr = db * 32 + (lane & 31);
+        const u32x2_t lo = *(const u32x2_t *)(&sm.Vt[dr * VTS + kbase]);
+        const u32x2_t hi = *(const u32x2_t *)(&sm.Vt[dr * VTS + kbase + 8]);
+        u32x4_t vw;
+        vw[0] = lo[0]; vw[1] = lo[1]; vw[2] = hi[0]; vw[3] = hi[1];
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pop,
+                                                           oacc[db], 0, 0, 0);
+      }
+    }
+  }
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!rvalid) return;
+  const float inv = 1.f / l_tot;
+  uint16_t *orow = a.o + (size_t)(it.row0 + tok) * a.ld_o + head * HD;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + g4 * 8 + half * 4;
+      if (d >= HD) continue;
+      uint2 wv;
+      wv.x = pack_bf2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv);
+      wv.y = pack_bf2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv);
+      *(uint2 *)(orow + d) = wv;
+    }
+}
+
+template <int HD, int G>
+__device__ void decode_path(const AttnArgs &a, const AttnWork &w) {
+  constexpr int LPK = HD / 8;              // lanes per key
+  constexpr int KPI = 64 / LPK;            // keys per load instruction
+  constexpr int NLD = KPI >= 16 ? 1 : 16 / KPI;
+  constexpr int BLK = KPI * NLD;           // keys per softmax block
+  constexpr int WSPAN = ATTN_SPLIT / ATTN_WAVES;
+  const DevItem it = a.items[w.item];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPK, kg = lane / LPK;
+  const int wk0 = w.k0 + wave * WSPAN;
+  const int wk1 = min(w.k1, wk0 + WSPAN);
+  const int32_t *pages = a.page_ids + it.page_off;
+
+  float q[G][8];
+  {
+    const uint16_t *qrow = a.qkv + (size_t)it.row0 * a.ld_qkv + (w.kvh * G) * HD + sub * 8;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const u32x4_t v = *(const u32x4_t *)(qrow + h * HD);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q[h][2 * e] = lo_bf(v[e]) * a.scale_log2;
+        q[h][2 * e + 1] = hi_bf(v[e]) * a.scale_log2;
+      }
+    }
+  }
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+  for (int kb = wk0; kb < wk1; kb += BLK) {
+    float sc[NLD][G];
+    u32x4_t vv[NLD];
+#pragma unroll
+    for (int li = 0; li < NLD; ++li) {
+      const int key = kb + li * KPI + kg;
+      const bool valid = key < wk1;
+      u32x4_t kv = {0u, 0u, 0u, 0u};
+      vv[li] = kv;
+      if (valid) {
+        const int page = pages[key / a.ps];
+        const size_t off = (((size_t)page * a.Hkv + w.kvh) * a.ps + key % a.ps) * HD + sub * 8;
+        kv = *(const u32x4_t *)(a.kc + off);
+        vv[li] = *(const u32x4_t *)(a.vc + off);
+      }
+      float kf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[2 * e] = lo_bf(kv[e]);
+        kf[2 * e + 1] = hi_bf(kv[e]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(q[h][e], kf[e], d);
+#pragma unroll
+        for (int o = 1; o < LPK; o <<= 1) d += __shfl_xor(d, o, 64);
+        sc[li][h] = valid ? d : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mb = sc[0][h];
+#pragma unroll
+      for (int li = 1; li < NLD; ++li) mb = fmaxf(mb, sc[li][h]);
+#pragma unroll
+      for (int o = LPK; o < 64; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o, 64));
+      const float m_new = fmaxf(m[h], mb);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2f(m[h] - m_use);
+      m[h] = m_new;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+#pragma unroll
+      for (int li = 0; li < NLD; ++li) {
+        const float p = exp2f(sc[li][h] - m_use);
+        l[h] += p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[h][2 * e] = fmaf(p, lo_bf(vv[li][e]), acc[h][2 * e]);
+          acc[h][2 * e + 1] = fmaf(p, hi_bf(vv[li][e]), acc[h][2 * e + 1]);
+        }
+      }
+    }
+  }
+  // sum the key groups (each LPK-lane group saw different keys)
+  const int pidx = w.part * ATTN_WAVES + wave;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float lt = l[h];
+#pragma unroll
+    for (int o = LPK; o < 64; o <<= 1) lt += __shfl_xor(lt, o, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+#pragma unroll
+      for (int o = LPK; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+      acc[h][e] = v;
+    }
+    if (kg == 0) {
+      float *dst = a.part_o + ((size_t)pidx * G + h) * HD + sub * 8;
+      *(float4 *)dst = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *(float4 *)(dst + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+    if (lane == 0) {
+      a.part_ml[((size_t)pidx * G + h) * 2 + 0] = m[h];
+      a.part_ml[((size_t)pidx * G + h) * 2 + 1] = lt;
+    }
+  }
+}
+
+template <int HD, int G>
+__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) ChunkSmem<HD> sm;
+  const AttnWork w = a.work[blockIdx.x];
+  if (w.type == WORK_CHUNK) chunk_path<HD>(a, w, sm);
+  else decode_path<HD, G>(a, w);
+}
+
+// Merge the split partials of each decode row: out = sum_p exp2(m_p - M) o_p /
+// sum_p exp2(m_p - M) l_p.  Grid (decode item, query head), HD threads.
+template <int HD>
+__global__ void attn_combine_kernel(const DevItem *items, const int32_t *dec_items, const float *part_ml,
+                                    const float *part_o, uint16_t *o, int ld_o, int G) {
+  const DevItem it = items[dec_items[blockIdx.x]];
+  const int h = blockIdx.y;
+  const int kvh = h / G, hh = h % G;
+  const int d = threadIdx.x;
+  const int p0 = (it.part0 + kvh * it.n_parts) * ATTN_WAVES;
+  const int np = it.n_parts * ATTN_WAVES;
+  float M = -INFINITY;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, part_ml[((size_t)(p0 + p) * G + hh) * 2]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f, acc = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const size_t idx = (size_t)(p0 + p) * G + hh;
+    const float wgt = exp2f(part_ml[idx * 2] - Mu);
+    L += wgt * part_ml[idx * 2 + 1];
+    acc += wgt * part_o[idx * HD + d];
+  }
+  o[(size_t)it.row0 * ld_o + h * HD + d] = (uint16_t)f2bf(acc / L);
+}
+
+template <int HD>
+static int launch_hd(const AttnArgs &a, int n_work, int G, hipStream_t s) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((attention_kernel<HD, 1>), dim3(n_work), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attention_kernel<HD, 2>), dim3(n_work), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attention_kernel<HD, 4>), dim3(n_work), dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((attention_kernel<HD, 8>), dim3(n_work), dim3(256), 0, s, a); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  ORTHRUS_LAUNCH_CHECK();
+  return 0;
+}
+
+int launch_attention(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
+                     const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
+                     float *part_ml, float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd,
+                     int ps, void *stream) {
+  if (n_work <= 0) return 0;
+  AttnArgs a;
+  a.qkv = qkv; a.kc = kc; a.vc = vc; a.page_ids = page_ids; a.items = items; a.work = work;
+  a.part_ml = part_ml; a.part_o = part_o; a.o = o;
+  a.ld_qkv = ld_qkv; a.ld_o = ld_o; a.Hq = Hq; a.Hkv = Hkv; a.ps = ps;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  const int G = Hq / Hkv;
+  hipStream_t s = (hipStream_t)stream;
+  switch (hd) {
+    case 16: return launch_hd<16>(a, n_work, G, s);
+    case 32: return launch_hd<32>(a, n_work, G, s);
+    case 64: return launch_hd<64>(a, n_work, G, s);
+    case 128: return launch_hd<128>(a, n_work, G, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_dec, const float *part_ml,
+                        const float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd,
+                        void *stream) {
+  if (n_dec <= 0) return 0;
+  const int G = Hq / Hkv;
+  hipStream_t s = (hipStream_t)stream;
+  dim3 grid(n_dec, Hq);
+  switch (hd) {
+    case 16: hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(16), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
+    case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, grid, dim3(32), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
+    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, grid, dim3(64), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
+    case 128: hipLaunchKernelGGL(attn_combine_kernel<128>, grid, dim3(128), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  ORTHRUS_LAUNCH_CHECK();
+  return 0;
+}
+
+}  // namespace orthrus

@@ -1,0 +1,78 @@
+// Internal declarations shared by the engine and the kernel launchers.
+#pragma once
+
+#include <stdint.h>
+#include <vector>
+
+#include "../../include/orthrus.h"
+
+namespace orthrus {
+
+struct HostPack {
+  int n_items = 0, n_tokens = 0;
+  std::vector<int32_t> cu_q, pos, slot, row_item, logit_rows, pool_segs;
+  int rows_by_kind[3] = {0, 0, 0};
+  int n_emb = 0;
+};
+
+orthrus_status validate_and_pack(const orthrus_model_cfg &cfg, const orthrus_batch &b,
+                                 HostPack &p, char *err, int32_t elen);
+
+// ---- attention work list -------------------------------------------------
+// One entry per workgroup of the ragged attention launch.
+//  CHUNK : rows [q0, q0+qn) of item `item` (local row indices) for KV head
+//          `kvh`, against keys [0, ctx + q0 + qn).
+//  DECODE: the decode row of `item` for KV head `kvh` against keys
+//          [k0, k1); each of the 4 waves writes partial `part*4 + wave`.
+enum { WORK_CHUNK = 0, WORK_DECODE = 1 };
+struct AttnWork {
+  int32_t type, item, kvh, q0, qn, k0, k1, part;
+};
+// Per-item device record used by the attention and combine kernels.
+struct DevItem {
+  int32_t row0, n, ctx, page_off, kind, part0, n_parts, pad;
+};
+
+constexpr int ATTN_ROWS = 128;       // (token, head) rows per chunk workgroup
+constexpr int ATTN_SPLIT = 256;      // keys per decode workgroup (64 per wave)
+constexpr int ATTN_WAVES = 4;
+
+void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const HostPack &p,
+                     std::vector<AttnWork> &work, std::vector<DevItem> &items, int &n_parts);
+
+// ---- kernel launchers (kernels_*.hip) -------------------------------------
+struct LoraArgs {
+  const uint16_t *U = nullptr;   // [rows][ldu] bf16, already scaled
+  int ldu = 0;
+  const uint16_t *Bx = nullptr;  // [N][r] expand matrix
+  int r = 0;
+  int rows = 0;                  // rows < `rows` get the delta
+  int sec1 = 0, sec2 = 0;        // column n in section 0 if n < sec1, 1 if < sec2, else 2
+};
+
+enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
+
+int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C, int ldc,
+                int M, int N, int K, int epi, int b_up_row, float alpha,
+                const LoraArgs *lora, void *stream);
+
+int launch_embed_gather(const int32_t *tok, const uint16_t *E, float *x, int T, int d,
+                        void *stream);
+int launch_rmsnorm(const float *x, const uint16_t *g, uint16_t *h, int T, int d, float eps,
+                   void *stream);
+int launch_rope_kv(uint16_t *qkv, const int32_t *pos, const int32_t *slot,
+                   const double *inv_freq, uint16_t *kc, uint16_t *vc, int T, int Hq, int Hkv,
+                   int hd, int ps, void *stream);
+int launch_attention(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
+                     const int32_t *page_ids, const DevItem *items, const AttnWork *work,
+                     int n_work, float *part_ml, float *part_o, uint16_t *o, int ld_o,
+                     int Hq, int Hkv, int hd, int ps, void *stream);
+int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_dec,
+                        const float *part_ml, const float *part_o, uint16_t *o, int ld_o,
+                        int Hq, int Hkv, int hd, void *stream);
+int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_rows, int n_embed,
+                      int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream);
+int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, float *wsum,
+                float *kept, float *emb, int d, void *stream);
+
+}  // namespace orthrus

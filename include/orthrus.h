@@ -1,0 +1,199 @@
+/*
+ * orthrus.h — C ABI of the MI355X heterogeneous-batch forward step.
+ *
+ * One call runs one forward pass of a pre-norm decoder (RMSNorm, GQA
+ * attention with rotate-half RoPE, SwiGLU FFN) over a packed, ragged batch
+ * that mixes embedding chunks, generation prefill chunks and single-token
+ * decode rows, then splits the outputs: next-token logits for generation,
+ * incremental pooling for embedding.  This is the runner's forward + emit
+ * stages as described in "Efficient Iterative Retrieval with Heterogeneous
+ * Batching" (paperpeel full text), §3.1 High-Level Workflow and §3.2 Batch
+ * Unit, with the pooling state of §3.3 Incremental Pooler as completed on
+ * the agihunt summary page (running weighted sum + weight total, or a kept
+ * hidden state).  A LoRA adapter applies to embedding rows only (§2.2
+ * Parameter sharing, §5.1 Workloads, Models, and Hardware).
+ *
+ * Conventions
+ *  - Every pointer documented "device" is device memory of the current HIP
+ *    device; "host" pointers are ordinary host memory.  The caller owns all
+ *    of them.  The engine owns only its workspace and pinned staging.
+ *  - bf16 is IEEE bfloat16 stored as 16-bit patterns; fp32 is IEEE binary32.
+ *  - Linear weights are row-major [out_features][in_features].
+ *  - K and V caches are each [n_layers][n_pages][n_kv_heads][page_size]
+ *    [head_dim] bf16.  Token position p of an item lives in page
+ *    page_ids[page_off + p / page_size] at in-page offset p % page_size.
+ *  - Nothing throws across this ABI.  Validation runs before any device
+ *    work; on a non-OK status no device memory has been touched.
+ */
+#ifndef ORTHRUS_H
+#define ORTHRUS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ORTHRUS_OK = 0,
+  ORTHRUS_EINVAL = 1,     /* malformed batch or configuration */
+  ORTHRUS_ENOPAGES = 2,   /* an item's pages cannot hold ctx_len + n_tokens, or a page id is out of range */
+  ORTHRUS_ECAPACITY = 3,  /* batch exceeds max_tokens/max_items, or an output buffer is too small */
+  ORTHRUS_ESTATE = 4,     /* pooling slot out of range or reused, or a first chunk not at position 0 */
+  ORTHRUS_ENOMEM = 5,     /* device or pinned allocation failed */
+  ORTHRUS_EHIP = 6        /* a HIP call failed; orthrus_last_error() has the HIP message */
+} orthrus_status;
+
+/* Item kinds, in the order a batch must list them (§3.2 Batch Unit: the
+ * scheduler emits batches sorted by request type). */
+enum { ORTHRUS_EMBED = 0, ORTHRUS_PREFILL = 1, ORTHRUS_DECODE = 2 };
+
+/* Pooling heads (§3.3 Incremental Pooler; agihunt summary).  MEAN weights
+ * every token 1; WMEAN weights a token by its 1-based position in the
+ * request; CLS keeps the hidden state at position 0; LAST keeps the hidden
+ * state of the request's final token. */
+enum { ORTHRUS_POOL_MEAN = 0, ORTHRUS_POOL_WMEAN = 1, ORTHRUS_POOL_CLS = 2, ORTHRUS_POOL_LAST = 3 };
+
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  int32_t lora_rank;       /* 0 = no adapter; otherwise a multiple of 8 */
+  int32_t page_size;       /* tokens per KV page */
+  int32_t n_pages;         /* pages in each layer's K and V pool */
+  int32_t max_tokens;      /* largest batch (rows) the engine accepts */
+  int32_t max_items;       /* largest item count the engine accepts */
+  int32_t max_pool_slots;  /* rows of the pooling state arrays */
+  float rope_theta, rms_eps, lora_scale;
+} orthrus_model_cfg;
+
+/* Per-layer weights, all device bf16.
+ *  w_qkv      [Hq*hd + 2*Hkv*hd][d]   q rows, then k rows, then v rows
+ *  w_o        [d][Hq*hd]
+ *  w_gate_up  [2*F][d]                gate rows, then up rows
+ *  w_down     [d][F]
+ *  g_attn, g_ffn [d]                  RMSNorm gains
+ *  lora_a_qkv [3*r][d]                shrink for q, k, v (r rows each)
+ *  lora_b_qkv [Hq*hd + 2*Hkv*hd][r]   expand; row n belongs to n's section
+ *  lora_a_o   [r][Hq*hd], lora_b_o [d][r]
+ * LoRA pointers may be NULL when lora_rank == 0. */
+typedef struct {
+  const void *w_qkv, *w_o, *w_gate_up, *w_down, *g_attn, *g_ffn;
+  const void *lora_a_qkv, *lora_b_qkv, *lora_a_o, *lora_b_o;
+} orthrus_layer_w;
+
+/* tok_emb [V][d], lm_head [V][d], g_final [d]: device bf16.
+ * layers: host array of n_layers entries (copied by orthrus_create). */
+typedef struct {
+  const void *tok_emb, *lm_head, *g_final;
+  const orthrus_layer_w *layers;
+} orthrus_weights;
+
+/* One batch item (host).  Rows of the batch follow item order.
+ *  kind        ORTHRUS_EMBED / PREFILL / DECODE; non-decreasing over items
+ *  req_id      unique within the batch
+ *  n_tokens    >= 1; exactly 1 for DECODE
+ *  ctx_len     tokens of this request already in the KV cache; the item's
+ *              rows sit at positions ctx_len .. ctx_len + n_tokens - 1
+ *  page_off, n_pages   the request's page list is page_ids[page_off ..
+ *              page_off + n_pages); n_pages * page_size >= ctx_len + n_tokens
+ *  pool_slot   EMBED only: row of the pooling state
+ *  pool_kind   EMBED only: ORTHRUS_POOL_*
+ *  is_first    EMBED: first chunk (resets the slot; requires ctx_len == 0)
+ *  is_last     EMBED: final chunk (emits the embedding); PREFILL: the chunk
+ *              completes the prompt (emits logits of its last row) */
+typedef struct {
+  int32_t kind, req_id, n_tokens, ctx_len, page_off, n_pages;
+  int32_t pool_slot, pool_kind, is_first, is_last;
+} orthrus_item;
+
+typedef struct {
+  int32_t n_items, n_tokens, n_page_ids;
+  const orthrus_item *items;   /* host [n_items] */
+  const int32_t *token_ids;    /* host [n_tokens], item order */
+  const int32_t *page_ids;     /* host [n_page_ids] */
+} orthrus_batch;
+
+/* Pooling state, device fp32: sum [max_pool_slots][d], wsum
+ * [max_pool_slots], kept [max_pool_slots][d].  Carried across steps by the
+ * caller; a slot is private to one request between its first and last
+ * chunk. */
+typedef struct {
+  float *sum, *wsum, *kept;
+} orthrus_pool_state;
+
+/* Host metadata produced by orthrus_pack (all host int32; caller-allocated
+ * with the capacities given in cap_tokens / cap_items).
+ *  cu_q       [n_items+1]  row offset of each item
+ *  pos        [n_tokens]   position of each row in its request
+ *  slot       [n_tokens]   KV slot written by each row: page * page_size + offset
+ *  row_item   [n_tokens]   item index of each row
+ *  logit_rows [n_items]    rows whose logits are emitted, in item order
+ *  pool_segs  [n_items*8]  per EMBED item: row_start, n_rows, pool_slot,
+ *                          pool_kind, is_first, is_last, ctx_len,
+ *                          output index (or -1 when not is_last) */
+typedef struct {
+  int32_t cap_tokens, cap_items;
+  int32_t *cu_q, *pos, *slot, *row_item, *logit_rows, *pool_segs;
+  int32_t n_embed_rows, n_prefill_rows, n_decode_rows, n_logits, n_emb, n_pool_segs;
+} orthrus_packed;
+
+typedef struct orthrus_engine orthrus_engine;
+
+/* Validate a batch against cfg and build its packing metadata; host only,
+ * no HIP call.  Checks run in a fixed order and the first failure is
+ * returned; err (may be NULL) receives a message.  Capacity of `out`
+ * arrays too small -> ORTHRUS_ECAPACITY. */
+orthrus_status orthrus_pack(const orthrus_model_cfg *cfg, const orthrus_batch *batch,
+                            orthrus_packed *out, char *err, int32_t err_len);
+
+/* Create an engine bound to the current HIP device.  Copies cfg and the
+ * weight pointer table; allocates the workspace for max_tokens/max_items.
+ * k_pages / v_pages: device bf16 KV pools (layout above), read and written
+ * by every step.  Returns EINVAL for unsupported shapes (head_dim not in
+ * {16,32,64,128}, n_q_heads not a multiple of n_kv_heads, d_model, Hq*hd,
+ * ffn_dim not multiples of 8, lora_rank not a multiple of 8), ENOMEM or
+ * EHIP on allocation failure. */
+orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weights *w,
+                              void *k_pages, void *v_pages, orthrus_engine **out);
+
+/* Run one step on `stream` (a hipStream_t; NULL = default stream).
+ * Asynchronous: outputs are valid once the stream has synchronised.  The
+ * batch's host arrays may be reused as soon as the call returns.
+ *  logits      device fp32 [logits_cap_rows][vocab]: rows in item order
+ *              (prefill items with is_last, then decode items)
+ *  emb         device fp32 [emb_cap_rows][d]: embedding items with is_last,
+ *              in item order (the pooled vector, not normalised)
+ *  n_logits, n_emb   host out: rows written
+ *  hidden_out  optional device fp32 [n_tokens][d]: residual stream after
+ *              the last layer (NULL to skip)
+ * Every row appends its K/V at its slot; pooling state is updated.
+ * Errors: any orthrus_pack status; ECAPACITY when logits_cap_rows or
+ * emb_cap_rows is too small; EHIP/ENOMEM from the runtime. */
+orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch,
+                            const orthrus_pool_state *pool, float *logits,
+                            int32_t logits_cap_rows, float *emb, int32_t emb_cap_rows,
+                            int32_t *n_logits, int32_t *n_emb, float *hidden_out,
+                            void *stream);
+
+/* Message of the last failed call on this engine ("" if none). */
+const char *orthrus_last_error(const orthrus_engine *eng);
+
+/* Free the engine's workspace.  Waits for its pending work. */
+void orthrus_destroy(orthrus_engine *eng);
+
+/* Standalone bf16 GEMM on the MFMA kernels of the step (device pointers):
+ *   C = A B^T with A [M][K] (lda), B [N][K] (ldb), fp32 accumulation.
+ * epilogue: 0 store C as bf16 [M][N] (ldc); 1 store fp32; 2 fp32 C += A B^T;
+ *           3 SwiGLU: B holds 2N rows at ldb (gate rows 0..N-1, up rows
+ *             N..2N-1 at row offset b_up_row), C bf16 = silu(gate) * up.
+ * K must be a multiple of 8.  Returns EINVAL for bad sizes, EHIP on
+ * launch failure.  Used by the step for the projections of the forward
+ * pass (§3.1: attention and feed-forward layers are shared by all items). */
+orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int32_t ldb,
+                                 void *C, int32_t ldc, int32_t M, int32_t N, int32_t K,
+                                 int32_t epilogue, int32_t b_up_row, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ORTHRUS_H */

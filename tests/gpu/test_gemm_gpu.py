@@ -1,0 +1,81 @@
+"""GEMM kernel parity: orthrus_gemm_bf16 against an fp64 matmul of the same
+bf16 operands (the definition C = A B^T), every epilogue, ragged edges."""
+
+import numpy as np
+import pytest
+import torch
+
+import heterogeneous_embed_decode_amd as hed
+from synth.bf16 import f32_to_bf16_bits, bf16_bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(rng, shape, scale=1.0):
+    bits = f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * scale)
+    return bits, bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _dev(bits):
+    return torch.from_numpy(bits.view(np.int16)).cuda()
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+SHAPES = [(34, 128, 64), (300, 176, 64), (129, 257, 176), (1, 64, 4096), (4160, 384, 512),
+          (64, 1000, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("epi", [hed.EPI_BF16, hed.EPI_F32, hed.EPI_RESID])
+def test_gemm_epilogues(M, N, K, epi):
+    print(f"gemm M={M} N={N} K={K} epi={epi}", flush=True)
+    rng = np.random.default_rng(M * 7 + N + K + epi)
+    a_bits, A = _bf16(rng, (M, K))
+    b_bits, B = _bf16(rng, (N, K), 0.05)
+    ref = A @ B.T
+    dA, dB = _dev(a_bits), _dev(b_bits)
+    if epi == hed.EPI_BF16:
+        C = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    else:
+        C = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    C0 = None
+    if epi == hed.EPI_RESID:
+        C0 = rng.standard_normal((M, N)).astype(np.float32)
+        C.copy_(torch.from_numpy(C0))
+        ref = ref + C0
+    st = hed.orthrus_gemm_bf16(dA.data_ptr(), K, dB.data_ptr(), K, C.data_ptr(), N, M, N, K, epi)
+    assert st == hed.OK
+    torch.cuda.synchronize()
+    if epi == hed.EPI_BF16:
+        got = bf16_bits_to_f32(C.cpu().numpy().view(np.uint16)).astype(np.float64)
+        tol = 8e-3
+    else:
+        got = C.cpu().numpy().astype(np.float64)
+        tol = 1e-5
+    assert _rel(got, ref) < tol
+
+
+@pytest.mark.parametrize("M,F,K", [(34, 176, 64), (257, 200, 128), (1024, 1024, 512)])
+def test_gemm_swiglu(M, F, K):
+    print(f"swiglu M={M} F={F} K={K}", flush=True)
+    rng = np.random.default_rng(M + F)
+    a_bits, A = _bf16(rng, (M, K))
+    b_bits, B = _bf16(rng, (2 * F, K), 0.1)
+    g = A @ B[:F].T
+    u = A @ B[F:].T
+    ref = g / (1 + np.exp(-g)) * u
+    C = torch.zeros((M, F), dtype=torch.int16, device="cuda")
+    st = hed.orthrus_gemm_bf16(_dev(a_bits).data_ptr(), K, _dev(b_bits).data_ptr(), K, C.data_ptr(), F,
+                               M, F, K, hed.EPI_SWIGLU, F)
+    assert st == hed.OK
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f32(C.cpu().numpy().view(np.uint16)).astype(np.float64)
+    assert _rel(got, ref) < 8e-3
+
+
+def test_gemm_rejects_bad_sizes():
+    assert hed.orthrus_gemm_bf16(1, 12, 1, 12, 1, 4, 4, 4, 12, 0) == hed.EINVAL
+    assert hed.orthrus_gemm_bf16(1, 16, 1, 16, 1, 4, 4, 4, 16, 9) == hed.EINVAL

@@ -1,0 +1,101 @@
+"""Whole-step parity through orthrus_step against the oracle: the small
+multi-step workload (prefill, then three mixed embedding/decode steps),
+LoRA and every pooling head, random ragged batches, the one-layer
+Mistral-7B-shaped batch, degenerate batches and host-side error paths."""
+
+import numpy as np
+import pytest
+import torch
+
+import heterogeneous_embed_decode_amd as hed
+from synth import model as sm
+from synth import workloads as wl
+from tests._gpu import make_pair, run_and_compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("pool_kind", [wl.POOL_MEAN, wl.POOL_WMEAN, wl.POOL_CLS, wl.POOL_LAST])
+def test_tiny_multistep(pool_kind):
+    cfg, batches, n_pages = wl.tiny_workload(pool_kind=pool_kind)
+    bits = sm.make_weights(cfg, seed=0, gain_std=0.1)
+    dev, orc = make_pair(cfg, n_pages, bits)
+    for s, b in enumerate(batches):
+        run_and_compare(cfg, dev, orc, b, tag=f"tiny pool={pool_kind} step={s}")
+    dev.close()
+
+
+def test_tiny_lora_mixed_heads():
+    cfg = sm.TINY.with_(lora_rank=8)
+    bits = sm.make_weights(cfg, seed=3, gain_std=0.1)
+    _, batches, n_pages = wl.tiny_workload(cfg=cfg, pool_kind=wl.POOL_WMEAN, chunk=7)
+    dev, orc = make_pair(cfg, n_pages, bits)
+    for s, b in enumerate(batches):
+        run_and_compare(cfg, dev, orc, b, tag=f"tiny-lora step={s}")
+    dev.close()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_ragged_batches(seed):
+    base = [sm.TINY.with_(lora_rank=8),
+            sm.ModelConfig(n_layers=1, d_model=128, n_q_heads=8, n_kv_heads=1, head_dim=32,
+                           ffn_dim=96, vocab=300, lora_rank=16, page_size=5, rope_theta=1e4),
+            sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=4, head_dim=64,
+                           ffn_dim=512, vocab=500, lora_rank=8, page_size=16, rope_theta=1e6),
+            sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                           ffn_dim=384, vocab=1000, lora_rank=16, page_size=16, rope_theta=1e6)][seed % 4]
+    b, n_pages = wl.random_batch(base, 100 + seed, max_items=15, max_len=150, max_ctx=700)
+    bits = sm.make_weights(base, seed=seed, gain_std=0.1)
+    kv = wl.synthetic_kv(base, n_pages, seed=3)
+    dev, orc = make_pair(base, n_pages, bits, kv_bits=kv)
+    run_and_compare(base, dev, orc, b, tag=f"random seed={seed}")
+    dev.close()
+
+
+def test_one_mistral_layer_full_batch():
+    cfg, batch, n_pages = wl.one_layer_workload()
+    print(f"one-layer: rows={batch.n_tokens} pages={n_pages}", flush=True)
+    bits = sm.make_weights(cfg, seed=0)
+    kv = wl.synthetic_kv(cfg, n_pages, seed=3)
+    dev, orc = make_pair(cfg, n_pages, bits, kv_bits=kv, max_tokens=8192, max_items=128)
+    run_and_compare(cfg, dev, orc, batch, tag="one-layer")
+    dev.close()
+
+
+def test_degenerate_batches_and_errors():
+    cfg = sm.TINY.with_(lora_rank=8)
+    bits = sm.make_weights(cfg, seed=1, gain_std=0.1)
+    n_pages = 40
+    dev, orc = make_pair(cfg, n_pages, bits)
+    # empty batch: nothing to do, OK
+    empty = wl.Batch([], np.zeros(0, np.int32), np.zeros(0, np.int32))
+    st, nl, ne = dev.step(empty)
+    assert (st, nl, ne) == (hed.OK, 0, 0)
+    # decode at context 0, a one-token embedding chunk, a one-token prefill
+    alloc = wl.PageAllocator(n_pages, seed=2)
+    bb = wl.BatchBuilder(cfg, alloc)
+    bb.add(wl.Request(1, wl.EMBED, [5], pool_slot=0, pool_kind=wl.POOL_CLS))
+    bb.add(wl.Request(2, wl.PREFILL, [7, 8]))
+    bb.add(wl.Request(3, wl.DECODE, [9]))
+    b = bb.build([(1, wl.EMBED, 1, 1, 1), (2, wl.PREFILL, 1, 1, 1), (3, wl.DECODE, 1, 0, 1)])
+    run_and_compare(cfg, dev, orc, b, tag="degenerate")
+    # invalid batch: error before any device work, KV untouched
+    before = dev.K.clone()
+    bad = wl.Batch([wl.Item(kind=wl.DECODE, req_id=1, n_tokens=1, ctx_len=0, page_off=0, n_pages=1),
+                    wl.Item(kind=wl.EMBED, req_id=2, n_tokens=1, ctx_len=0, page_off=1, n_pages=1,
+                            pool_slot=0, is_first=1, is_last=1)],
+                   np.array([1, 2], np.int32), np.array([3, 4], np.int32))
+    st, _, _ = dev.step(bad)
+    assert st == hed.EINVAL
+    assert "sorted" in hed.orthrus_last_error(dev.eng)
+    torch.cuda.synchronize()
+    assert torch.equal(before, dev.K)
+    # output capacity
+    small = wl.Batch([wl.Item(kind=wl.DECODE, req_id=i, n_tokens=1, ctx_len=0, page_off=i, n_pages=1)
+                      for i in range(3)], np.array([1, 2, 3], np.int32), np.array([0, 1, 2], np.int32))
+    a = dev.step_args(small)
+    st, _, _ = hed.orthrus_step(dev.eng, a, dev.pool_sum.data_ptr(), dev.pool_wsum.data_ptr(),
+                                dev.pool_kept.data_ptr(), dev.logits.data_ptr(), 2, dev.emb.data_ptr(),
+                                4, None, None)
+    assert st == hed.ECAPACITY
+    dev.close()
