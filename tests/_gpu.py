@@ -29,6 +29,23 @@ def make_pair(dims, n_pages, weights, kv_bits=None, max_tokens=None, max_items=6
     return dev, (W, kv, pool)
 
 
+def seed_pool(dev, orc, seed=5):
+    """Same synthetic prior pooling state on both sides (mid-request chunks)."""
+    import torch
+    W, kv, pool = orc
+    rng = np.random.default_rng(seed)
+    S, d = pool["sum"].shape
+    sm_ = rng.standard_normal((S, d)).astype(np.float32) * 10
+    ws = rng.integers(1, 500, S).astype(np.float32)
+    kp = rng.standard_normal((S, d)).astype(np.float32)
+    pool["sum"][:] = sm_
+    pool["wsum"][:] = ws
+    pool["kept"][:] = kp
+    dev.pool_sum[:S].copy_(torch.from_numpy(sm_))
+    dev.pool_wsum[:S].copy_(torch.from_numpy(ws))
+    dev.pool_kept[:S].copy_(torch.from_numpy(kp))
+
+
 def run_and_compare(dims, dev, orc, batch, check_kv=True, dtype=np.float32, tag=""):
     W, kv, pool = orc
     print(f"[step {tag}] items={batch.n_items} rows={batch.n_tokens}", flush=True)

@@ -68,7 +68,8 @@ def test_gemm_swiglu(M, F, K):
     u = A @ B[F:].T
     ref = g / (1 + np.exp(-g)) * u
     C = torch.zeros((M, F), dtype=torch.int16, device="cuda")
-    st = hed.orthrus_gemm_bf16(_dev(a_bits).data_ptr(), K, _dev(b_bits).data_ptr(), K, C.data_ptr(), F,
+    dA, dB = _dev(a_bits), _dev(b_bits)   # keep both alive across the launch
+    st = hed.orthrus_gemm_bf16(dA.data_ptr(), K, dB.data_ptr(), K, C.data_ptr(), F,
                                M, F, K, hed.EPI_SWIGLU, F)
     assert st == hed.OK
     torch.cuda.synchronize()

@@ -10,7 +10,7 @@ import torch
 import heterogeneous_embed_decode_amd as hed
 from synth import model as sm
 from synth import workloads as wl
-from tests._gpu import make_pair, run_and_compare
+from tests._gpu import make_pair, run_and_compare, seed_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,7 @@ def test_random_ragged_batches(seed):
     bits = sm.make_weights(base, seed=seed, gain_std=0.1)
     kv = wl.synthetic_kv(base, n_pages, seed=3)
     dev, orc = make_pair(base, n_pages, bits, kv_bits=kv)
+    seed_pool(dev, orc, seed)
     run_and_compare(base, dev, orc, b, tag=f"random seed={seed}")
     dev.close()
 
