@@ -67,7 +67,7 @@ class orthrus_packed(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m heterogeneous_embed_decode_amd.build`")
+                          "`python heterogeneous_embed_decode_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     lib.orthrus_pack.argtypes = [ctypes.POINTER(orthrus_model_cfg), ctypes.POINTER(orthrus_batch),
                                  ctypes.POINTER(orthrus_packed), ctypes.c_char_p, _i32]
@@ -84,12 +84,16 @@ def _load():
     lib.orthrus_destroy.restype = None
     lib.orthrus_gemm_bf16.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.orthrus_gemm_bf16.restype = ctypes.c_int
+    lib.orthrus_profile.argtypes = [_vp, _i32]
+    lib.orthrus_profile.restype = ctypes.c_int
+    lib.orthrus_profile_read.argtypes = [_vp, ctypes.c_char_p, _i32]
+    lib.orthrus_profile_read.restype = _i32
     return lib
 
 
 LIB = _load()
 EXPORTS = ("orthrus_pack", "orthrus_create", "orthrus_step", "orthrus_last_error",
-           "orthrus_destroy", "orthrus_gemm_bf16")
+           "orthrus_destroy", "orthrus_gemm_bf16", "orthrus_profile", "orthrus_profile_read")
 
 
 class OrthrusError(RuntimeError):
@@ -180,3 +184,17 @@ def orthrus_destroy(eng) -> None:
 
 def orthrus_gemm_bf16(A, lda, B, ldb, C, ldc, M, N, K, epilogue, b_up_row=0, stream=None) -> int:
     return LIB.orthrus_gemm_bf16(A, lda, B, ldb, C, ldc, M, N, K, epilogue, b_up_row, stream)
+
+
+def orthrus_profile(eng, enable: bool) -> int:
+    return LIB.orthrus_profile(eng, 1 if enable else 0)
+
+
+def orthrus_profile_read(eng) -> dict:
+    import json
+    n = LIB.orthrus_profile_read(eng, None, 0)
+    if n < 0:
+        raise OrthrusError(EINVAL, "null engine")
+    buf = ctypes.create_string_buffer(n + 1)
+    LIB.orthrus_profile_read(eng, buf, n + 1)
+    return json.loads(buf.value.decode())

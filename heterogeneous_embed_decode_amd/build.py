@@ -1,6 +1,6 @@
 """Build liborthrus.so in-tree with hipcc for gfx950.
 
-    python -m heterogeneous_embed_decode_amd.build
+    python heterogeneous_embed_decode_amd/build.py
 
 Compiles every source under csrc/ to an object (in parallel) and links
 ``_lib/liborthrus.so``.  Packed-fp32 instructions are disabled in device

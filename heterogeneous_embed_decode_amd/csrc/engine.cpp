@@ -34,6 +34,14 @@ struct orthrus_engine {
   hipEvent_t staged{};
   bool staged_pending = false;
   std::string err;
+  // per-kernel event timing (opt-in)
+  bool profiling = false;
+  struct Mark {
+    const char *name;
+    hipEvent_t a, b;
+  };
+  std::vector<Mark> marks;
+  std::vector<hipEvent_t> ev_free;
   // scratch host vectors
   HostPack pack;
   std::vector<AttnWork> work;
@@ -53,10 +61,32 @@ orthrus_status hip_fail(orthrus_engine *e, hipError_t r, const char *what) {
     if (r_ != hipSuccess) return hip_fail(eng, r_, what); \
   } while (0)
 
-#define LCHK(call, what)                                               \
-  do {                                                                 \
-    int r_ = (call);                                                   \
-    if (r_ != 0) return hip_fail(eng, (hipError_t)r_, what);           \
+hipEvent_t take_event(orthrus_engine *e) {
+  if (!e->ev_free.empty()) {
+    hipEvent_t ev = e->ev_free.back();
+    e->ev_free.pop_back();
+    return ev;
+  }
+  hipEvent_t ev{};
+  if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+  return ev;
+}
+
+// Launch `call`; when profiling, bracket it with events on the step stream.
+#define LCHK(call, what)                                                  \
+  do {                                                                    \
+    hipEvent_t ea_ = nullptr, eb_ = nullptr;                              \
+    if (eng->profiling) {                                                 \
+      ea_ = take_event(eng);                                              \
+      eb_ = take_event(eng);                                              \
+      if (ea_) (void)hipEventRecord(ea_, s);                              \
+    }                                                                     \
+    int r_ = (call);                                                      \
+    if (r_ != 0) return hip_fail(eng, (hipError_t)r_, what);              \
+    if (ea_ && eb_) {                                                     \
+      (void)hipEventRecord(eb_, s);                                       \
+      eng->marks.push_back({what, ea_, eb_});                             \
+    }                                                                     \
   } while (0)
 
 size_t align4(size_t n) { return (n + 3) & ~(size_t)3; }
@@ -114,6 +144,13 @@ extern "C" {
 const char *orthrus_last_error(const orthrus_engine *eng) { return eng ? eng->err.c_str() : ""; }
 
 static void free_all(orthrus_engine *e) {
+  for (auto &m : e->marks) {
+    (void)hipEventDestroy(m.a);
+    (void)hipEventDestroy(m.b);
+  }
+  e->marks.clear();
+  for (auto ev : e->ev_free) (void)hipEventDestroy(ev);
+  e->ev_free.clear();
   void *ptrs[] = {e->x, e->h, e->qkv, e->o, e->act, e->U, e->hf, e->hl, e->inv_freq,
                   e->part_ml, e->part_o, e->meta_dev};
   for (void *p : ptrs)
@@ -363,6 +400,54 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   if (n_segs)
     LCHK(launch_pool(eng->hf, d_segs, (int)n_segs, pool->sum, pool->wsum, pool->kept, emb, d, s), "pool");
   return ORTHRUS_OK;
+}
+
+orthrus_status orthrus_profile(orthrus_engine *eng, int32_t enable) {
+  if (!eng) return ORTHRUS_EINVAL;
+  eng->profiling = enable != 0;
+  return ORTHRUS_OK;
+}
+
+int32_t orthrus_profile_read(orthrus_engine *eng, char *json, int32_t len) {
+  if (!eng) return -1;
+  struct Acc {
+    std::string name;
+    int count = 0;
+    double ms = 0, min_ms = 1e30, max_ms = 0;
+  };
+  std::vector<Acc> acc;
+  for (auto &m : eng->marks) {
+    float ms = 0.f;
+    if (hipEventSynchronize(m.b) != hipSuccess || hipEventElapsedTime(&ms, m.a, m.b) != hipSuccess) ms = -1.f;
+    eng->ev_free.push_back(m.a);
+    eng->ev_free.push_back(m.b);
+    Acc *a = nullptr;
+    for (auto &x : acc)
+      if (x.name == m.name) a = &x;
+    if (!a) {
+      acc.push_back(Acc{m.name});
+      a = &acc.back();
+    }
+    a->count++;
+    a->ms += ms;
+    a->min_ms = std::min(a->min_ms, (double)ms);
+    a->max_ms = std::max(a->max_ms, (double)ms);
+  }
+  eng->marks.clear();
+  std::string out = "{";
+  for (size_t i = 0; i < acc.size(); ++i) {
+    char buf[256];
+    snprintf(buf, sizeof buf, "%s\"%s\": {\"count\": %d, \"total_ms\": %.6f, \"min_ms\": %.6f, \"max_ms\": %.6f}",
+             i ? ", " : "", acc[i].name.c_str(), acc[i].count, acc[i].ms, acc[i].min_ms, acc[i].max_ms);
+    out += buf;
+  }
+  out += "}";
+  if (json && len > 0) {
+    const size_t n = std::min(out.size(), (size_t)len - 1);
+    memcpy(json, out.data(), n);
+    json[n] = 0;
+  }
+  return (int32_t)out.size();
 }
 
 orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int32_t ldb, void *C, int32_t ldc,

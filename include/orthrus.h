@@ -180,6 +180,17 @@ const char *orthrus_last_error(const orthrus_engine *eng);
 /* Free the engine's workspace.  Waits for its pending work. */
 void orthrus_destroy(orthrus_engine *eng);
 
+/* Per-kernel timing.  While enabled, every kernel launch of orthrus_step is
+ * bracketed by HIP events recorded on the step's stream (the stream the
+ * kernel runs on).  orthrus_profile_read waits for the recorded events,
+ * writes a JSON object {"<kernel>": {"count", "total_ms", "min_ms",
+ * "max_ms"}, ...} accumulated since the last read into json (truncated to
+ * len-1 bytes, NUL-terminated), clears the record and returns the full
+ * length, or -1 for a NULL engine.  Host-side instrumentation only; the
+ * kernels are unchanged. */
+orthrus_status orthrus_profile(orthrus_engine *eng, int32_t enable);
+int32_t orthrus_profile_read(orthrus_engine *eng, char *json, int32_t len);
+
 /* Standalone bf16 GEMM on the MFMA kernels of the step (device pointers):
  *   C = A B^T with A [M][K] (lda), B [N][K] (ldb), fp32 accumulation.
  * epilogue: 0 store C as bf16 [M][N] (ldc); 1 store fp32; 2 fp32 C += A B^T;

@@ -7,6 +7,8 @@ Norm gains are 1 unless ``gain_std`` is set, in which case they are
 """
 
 from dataclasses import dataclass, asdict, replace
+import concurrent.futures as cf
+import os
 import zlib
 
 import numpy as np
@@ -95,18 +97,47 @@ def _tensor_seed(seed: int, name: str) -> int:
     return (int(seed) * 1000003 + zlib.crc32(name.encode())) & 0x7FFFFFFF
 
 
+CHUNK = 1 << 22
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        _POOL = cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4))
+    return _POOL
+
+
+def normal_bf16(key, n: int, std: float, mean: float = 0.0) -> np.ndarray:
+    """n values mean + N(0, std), rounded to bf16 bits.  Generated in chunks of
+    2^22 values, chunk i from numpy's PCG64 seeded with (key..., i), so the
+    result depends only on (key, n, std, mean)."""
+    out = np.empty(n, np.uint16)
+    key = list(key)
+
+    def work(i):
+        m = min(CHUNK, n - i * CHUNK)
+        v = np.random.default_rng(key + [i]).standard_normal(m, dtype=np.float32)
+        v *= np.float32(std)
+        if mean:
+            v += np.float32(mean)
+        out[i * CHUNK: i * CHUNK + m] = f32_to_bf16_bits(v)
+
+    list(_pool().map(work, range((n + CHUNK - 1) // CHUNK)))
+    return out
+
+
 def make_tensor(seed: int, name: str, shape, std: float = 0.02,
                 gain_std: float = 0.0) -> np.ndarray:
     """One seeded tensor as uint16 bf16 bits."""
-    rng = np.random.default_rng(_tensor_seed(seed, name))
+    n = int(np.prod(shape)) if len(shape) else 1
+    key = [_tensor_seed(seed, name)]
     base = name.split(".")[-1]
     if base.startswith("g_"):
-        v = np.ones(shape, np.float32)
-        if gain_std:
-            v += rng.standard_normal(shape, dtype=np.float32) * np.float32(gain_std)
-    else:
-        v = rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
-    return f32_to_bf16_bits(v)
+        if not gain_std:
+            return f32_to_bf16_bits(np.ones(shape, np.float32))
+        return normal_bf16(key, n, gain_std, mean=1.0).reshape(shape)
+    return normal_bf16(key, n, std).reshape(shape)
 
 
 def make_weights(cfg: ModelConfig, seed: int = 0, std: float = 0.02,

@@ -256,10 +256,10 @@ def kv_pool_shape(cfg: ModelConfig, n_pages: int):
 
 
 def synthetic_kv(cfg: ModelConfig, n_pages: int, seed: int = 3):
-    """Seeded prior KV content for the whole pool, as uint16 bf16 bits."""
-    from .bf16 import f32_to_bf16_bits
-    rng = np.random.default_rng(seed)
+    """Seeded prior KV content (unit normal) for the whole pool, as uint16 bf16 bits."""
+    from .model import normal_bf16
     shape = kv_pool_shape(cfg, n_pages)
-    k = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
-    v = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    n = int(np.prod(shape))
+    k = normal_bf16([seed, 0], n, 1.0).reshape(shape)
+    v = normal_bf16([seed, 1], n, 1.0).reshape(shape)
     return k, v
