@@ -416,11 +416,14 @@ int32_t orthrus_profile_read(orthrus_engine *eng, char *json, int32_t len) {
     double ms = 0, min_ms = 1e30, max_ms = 0;
   };
   std::vector<Acc> acc;
+  const bool consume = json != nullptr && len > 0;
   for (auto &m : eng->marks) {
     float ms = 0.f;
     if (hipEventSynchronize(m.b) != hipSuccess || hipEventElapsedTime(&ms, m.a, m.b) != hipSuccess) ms = -1.f;
-    eng->ev_free.push_back(m.a);
-    eng->ev_free.push_back(m.b);
+    if (consume) {
+      eng->ev_free.push_back(m.a);
+      eng->ev_free.push_back(m.b);
+    }
     Acc *a = nullptr;
     for (auto &x : acc)
       if (x.name == m.name) a = &x;
@@ -433,7 +436,7 @@ int32_t orthrus_profile_read(orthrus_engine *eng, char *json, int32_t len) {
     a->min_ms = std::min(a->min_ms, (double)ms);
     a->max_ms = std::max(a->max_ms, (double)ms);
   }
-  eng->marks.clear();
+  if (consume) eng->marks.clear();
   std::string out = "{";
   for (size_t i = 0; i < acc.size(); ++i) {
     char buf[256];

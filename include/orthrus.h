@@ -186,7 +186,8 @@ void orthrus_destroy(orthrus_engine *eng);
  * writes a JSON object {"<kernel>": {"count", "total_ms", "min_ms",
  * "max_ms"}, ...} accumulated since the last read into json (truncated to
  * len-1 bytes, NUL-terminated), clears the record and returns the full
- * length, or -1 for a NULL engine.  Host-side instrumentation only; the
+ * length, or -1 for a NULL engine.  With json NULL or len 0 it only returns
+ * the length and keeps the record.  Host-side instrumentation only; the
  * kernels are unchanged. */
 orthrus_status orthrus_profile(orthrus_engine *eng, int32_t enable);
 int32_t orthrus_profile_read(orthrus_engine *eng, char *json, int32_t len);
