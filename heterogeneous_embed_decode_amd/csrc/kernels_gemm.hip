@@ -10,8 +10,9 @@
 // rows below the embedding-row count, so generation rows never see it.
 //
 // Tiling: BM x BN output tile per workgroup of WM x WN waves, K-steps of
-// 64 staged through LDS with an XOR swizzle of 16-byte chunks, double
-// buffered; each wave issues v_mfma_f32_32x32x16_bf16 on 32x32 blocks.
+// BK fetched by buffer loads straight into LDS (XOR swizzle of 16-byte
+// chunks, an S-stage ring), each wave issuing v_mfma_f32_32x32x16_bf16 on
+// 32x32 blocks.  Operands must be smaller than 2 GiB (32-bit buffer offsets).
 #include "device_common.h"
 #include "orthrus_internal.h"
 
@@ -29,27 +30,57 @@ struct GemmArgs {
   int ldu, r, lrows, sec1, sec2;
 };
 
-constexpr int BK = 64;
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// LDS swizzle of the 16-byte chunks of one tile row (BK/8 chunks).
+// ds_read_b128 is served 16 lanes at a time across 64 banks (256 bytes);
+// the 16 rows a half-wave reads must land on 16 distinct 16-byte bank
+// slots.  A 128-byte row (BK = 64) has 8 chunks, so the chunk is XORed
+// with bits 1..3 of the row; a 64-byte row (BK = 32) has 4 chunks, XORed
+// with bits 2..3.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most `tiles_after` tiles of LPT loads per lane are in flight
+template <int LPT, int S>
+__device__ __forceinline__ void wait_tiles(int tiles_after) {
+  if (S >= 4 && tiles_after >= 2) wait_vmcnt<(S >= 4 ? 2 : 0) * LPT>();
+  else if (S >= 3 && tiles_after >= 1) wait_vmcnt<(S >= 3 ? 1 : 0) * LPT>();
+  else wait_vmcnt<0>();
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int S, int EPI>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
-  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
+  constexpr int NT = NW * 64;
   constexpr int BNB = DUAL ? 2 * BN : BN;      // B rows staged per tile
   constexpr int WTM = BM / WM;                  // wave tile rows
   constexpr int WCN = BN / WN;                  // wave tile output columns
   constexpr int MI = WTM / 32;
   constexpr int NI = DUAL ? 2 * (WCN / 32) : WCN / 32;
-  constexpr int A_LD = BM * (BK / 8) / NT;
-  constexpr int B_LD = BNB * (BK / 8) / NT;
-  static_assert(A_LD * NT == BM * BK / 8 && B_LD * NT == BNB * BK / 8, "tile/threads mismatch");
+  constexpr int CPR = BK / 8;                   // 16-byte chunks per tile row
+  constexpr int RPI = 64 / CPR;                 // tile rows per wave load instruction
+  constexpr int A_ROUNDS = BM / (RPI * NW);
+  constexpr int B_ROUNDS = BNB / (RPI * NW);
+  constexpr int LPT = A_ROUNDS + B_ROUNDS;      // loads per lane per tile
+  static_assert(A_ROUNDS * RPI * NW == BM && B_ROUNDS * RPI * NW == BNB, "tile/threads mismatch");
+  static_assert(S >= 2 && S <= 4, "2..4 stages");
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BNB * BK];
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t *const As0 = smem;                   // [S][BM * BK]
+  uint16_t *const Bs0 = smem + S * BM * BK;     // [S][BNB * BK]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   // tile order: XCD-contiguous ranges, then groups of GM tile rows walked
@@ -79,8 +110,6 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-
   // B tile row rr -> output column of that row and its global B row
   auto b_src_row = [&](int rr, int &ncol) -> int {
     if (DUAL) {
@@ -92,91 +121,130 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     return ncol;
   };
 
+  // Operand tiles are fetched with buffer loads that write straight into
+  // LDS (16 bytes per lane, lane t of a wave at M0 + 16 t).  The XOR swizzle
+  // is applied on the global side: the lane that fills LDS chunk (row, pc)
+  // fetches logical chunk pc ^ swz(row).  Rows or K-chunks outside the
+  // operand get an out-of-range offset, which the buffer unit returns as
+  // zeros, so the loop has no branches.
+  constexpr uint32_t OOB = 0x80000000u;
+  const int lrow = lane / CPR, pc = lane % CPR;
+
+  // MFMA operand fragments of one 16-wide k slice
+  auto load_frags = [&](const uint16_t *As, const uint16_t *Bs, int kk, bf16x8_t *a, bf16x8_t *b) {
+    const int chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int row = wm * WTM + i * 32 + (lane & 31);
+      a[i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(&As[row * BK + ((chunk ^ swz<BK>(row)) * 8)]));
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      int rr;
+      if (DUAL)
+        rr = (j < NI / 2 ? 0 : BN) + wn * WCN + (j % (NI / 2)) * 32 + (lane & 31);
+      else
+        rr = wn * WCN + j * 32 + (lane & 31);
+      b[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(&Bs[rr * BK + ((chunk ^ swz<BK>(rr)) * 8)]));
+    }
+  };
+  // all k slices of one stage; fragments of slice k+1 are read before the
+  // MFMAs of slice k are issued so LDS latency hides behind matrix work
+  auto compute = [&](int st) {
+    const uint16_t *As = As0 + st * BM * BK, *Bs = Bs0 + st * BNB * BK;
+    bf16x8_t a[2][MI], b[2][NI];
+    load_frags(As, Bs, 0, a[0], b[0]);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // phase 0: main operands over K; phase 1: adapter operands over ldu
   auto run_phase = [&](const int phase, const int Kp) {
-    u32x4_t ra[A_LD], rb[B_LD];
-    auto gload = [&](int k0) {
+    const uint16_t *abase = phase == 0 ? g.A : g.U;
+    const int alda = phase == 0 ? g.lda : g.ldu;
+    const int arows = phase == 0 ? g.M : min(g.M, g.lrows);
+    const uint16_t *bbase = phase == 0 ? g.B : g.Bx;
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void *)abase, (short)0, (int)0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)bbase, (short)0, (int)0x7fffffff, 0x00020000);
+    // per-lane byte offsets at k0 = 0 (OOB when the row is outside)
+    uint32_t aoff[A_ROUNDS], boff[B_ROUNDS];
+    int akc[A_ROUNDS], bkc[B_ROUNDS];
 #pragma unroll
-      for (int i = 0; i < A_LD; ++i) {
-        const int c = tid + i * NT;
-        const int row = c / (BK / 8), kc = c % (BK / 8);
-        const int gr = m0 + row, k = k0 + kc * 8;
-        if (phase == 0)
-          ra[i] = (gr < g.M && k < Kp) ? *(const u32x4_t *)(g.A + (size_t)gr * g.lda + k) : zero4;
-        else
-          ra[i] = (gr < g.lrows && gr < g.M && k < Kp) ? *(const u32x4_t *)(g.U + (size_t)gr * g.ldu + k)
-                                                         : zero4;
+    for (int i = 0; i < A_ROUNDS; ++i) {
+      const int row = (i * NW + wave) * RPI + lrow;
+      const int kc = pc ^ swz<BK>(row);
+      const int gr = m0 + row;
+      akc[i] = kc * 8;
+      aoff[i] = gr < arows ? (uint32_t)(((size_t)gr * alda + kc * 8) * 2) : OOB;
+    }
+#pragma unroll
+    for (int i = 0; i < B_ROUNDS; ++i) {
+      const int rr = (i * NW + wave) * RPI + lrow;
+      const int kc = pc ^ swz<BK>(rr);
+      int ncol;
+      const int br = b_src_row(rr, ncol);
+      if (phase == 0) {
+        bkc[i] = kc * 8;
+        boff[i] = ncol < g.N ? (uint32_t)(((size_t)br * g.ldb + kc * 8) * 2) : OOB;
+      } else {
+        // adapter expand: column ncol holds s*B for its own section only;
+        // element k of the extension is B[ncol][k - sec*r] when that is in [0, r)
+        const int sec = ncol < g.sec1 ? 0 : (ncol < g.sec2 ? 1 : 2);
+        bkc[i] = kc * 8 - sec * g.r;
+        boff[i] = ncol < g.N ? (uint32_t)(((size_t)ncol * g.r + kc * 8 - sec * g.r) * 2) : OOB;
+      }
+    }
+    auto issue = [&](int kt) {
+      const int k0 = kt * BK, st = kt % S;
+#pragma unroll
+      for (int i = 0; i < A_ROUNDS; ++i) {
+        const bool ok = (k0 + akc[i]) < Kp && aoff[i] != OOB;
+        const uint32_t off = ok ? aoff[i] + (uint32_t)(k0 * 2) : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (lds_ptr_t)(As0 + st * BM * BK + (i * NW + wave) * 512), 16, off, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < B_LD; ++i) {
-        const int c = tid + i * NT;
-        const int rr = c / (BK / 8), kc = c % (BK / 8);
-        const int k = k0 + kc * 8;
-        int ncol;
-        const int br = b_src_row(rr, ncol);
-        if (phase == 0) {
-          rb[i] = (ncol < g.N && k < Kp) ? *(const u32x4_t *)(g.B + (size_t)br * g.ldb + k) : zero4;
-        } else {
-          const int sec = ncol < g.sec1 ? 0 : (ncol < g.sec2 ? 1 : 2);
-          const bool ok = ncol < g.N && k < Kp && (k / g.r) == sec;
-          rb[i] = ok ? *(const u32x4_t *)(g.Bx + (size_t)ncol * g.r + (k % g.r)) : zero4;
-        }
-      }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) {
-        const int c = tid + i * NT;
-        const int row = c / (BK / 8), kc = c % (BK / 8);
-        *(u32x4_t *)(&As[buf][row * BK + ((kc ^ (row & 7)) * 8)]) = ra[i];
-      }
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) {
-        const int c = tid + i * NT;
-        const int rr = c / (BK / 8), kc = c % (BK / 8);
-        *(u32x4_t *)(&Bs[buf][rr * BK + ((kc ^ (rr & 7)) * 8)]) = rb[i];
+      for (int i = 0; i < B_ROUNDS; ++i) {
+        bool ok = boff[i] != OOB;
+        if (phase == 0) ok = ok && (k0 + bkc[i]) < Kp;
+        else ok = ok && (k0 + bkc[i]) >= 0 && (k0 + bkc[i]) < g.r;
+        const uint32_t off = ok ? boff[i] + (uint32_t)(k0 * 2) : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (lds_ptr_t)(Bs0 + st * BNB * BK + (i * NW + wave) * 512), 16, off, 0, 0, 0);
       }
     };
     const int nk = (Kp + BK - 1) / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
+    // S-stage ring: tiles kt+1 .. kt+S-2 stay in flight while tile kt is
+    // consumed; one barrier per tile both publishes tile kt and retires
+    // the stage that the next issue overwrites.  The bare s_barrier avoids
+    // the fence of __syncthreads, which would drain the loads in flight.
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+      if (p < nk) issue(p);
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * BK);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int chunk = kk * 2 + (lane >> 5);
-        bf16x8_t a[MI], b[NI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const int row = wm * WTM + i * 32 + (lane & 31);
-          a[i] = __builtin_bit_cast(bf16x8_t,
-                                    *(const u32x4_t *)(&As[cur][row * BK + ((chunk ^ (row & 7)) * 8)]));
-        }
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          int rr;
-          if (DUAL)
-            rr = (j < NI / 2 ? 0 : BN) + wn * WCN + (j % (NI / 2)) * 32 + (lane & 31);
-          else
-            rr = wn * WCN + j * 32 + (lane & 31);
-          b[j] = __builtin_bit_cast(bf16x8_t,
-                                    *(const u32x4_t *)(&Bs[cur][rr * BK + ((chunk ^ (rr & 7)) * 8)]));
-        }
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NI; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-      if (kt + 1 < nk) sstore(cur ^ 1);
-      __syncthreads();
+      wait_tiles<LPT, S>(min(S - 2, nk - 1 - kt));
+      __builtin_amdgcn_s_barrier();
+      if (kt + S - 1 < nk) issue(kt + S - 1);
+      compute(kt % S);
     }
   };
 
   run_phase(0, g.K);
-  if (!DUAL && g.U != nullptr && m0 < g.lrows) run_phase(1, g.ldu);
+  if (!DUAL && g.U != nullptr && m0 < g.lrows) {
+    __builtin_amdgcn_s_barrier();  // all waves are done with the last stage
+    run_phase(1, g.ldu);
+  }
 
   // epilogue: lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane/32) + e%4
   const int jc = lane & 31;
@@ -193,8 +261,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
           const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
           if (m >= g.M) continue;
           const float gt = acc[i][j][e], up = acc[i][j + NI / 2][e];
-          const float s = gt / (1.f + expf(-gt));
-          ((uint16_t *)g.C)[(size_t)m * g.ldc + n] = (uint16_t)f2bf(s * up);
+          const float sg = gt / (1.f + expf(-gt));
+          ((uint16_t *)g.C)[(size_t)m * g.ldc + n] = (uint16_t)f2bf(sg * up);
         }
       }
     } else {
@@ -217,11 +285,20 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int S, int EPI>
 static int launch_cfg(const GemmArgs &a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (tiles == 0) return 0;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(tiles), dim3(WM * WN * 64), 0, s, a);
+  constexpr int BNB = (EPI == EPI_SWIGLU) ? 2 * BN : BN;
+  constexpr size_t lds = (size_t)S * (BM + BNB) * BK * sizeof(uint16_t);
+  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, BK, S, EPI>;
+  static bool attr_set = false;  // per process; the library drives one device at a time
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return (int)e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(WM * WN * 64), lds, s, a);
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }
@@ -239,11 +316,18 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
     a.sec1 = lora->sec1; a.sec2 = lora->sec2;
   }
   hipStream_t s = (hipStream_t)stream;
+  // Tile shapes measured on MI355X for the decoder's projections: 256-row
+  // tiles on 8 waves (two per SIMD) for wide outputs; 128x128 on 4 waves for
+  // the residual projections (more tiles, better balance over 256 CUs) and
+  // for small problems.
+  const bool big = M >= 512 && N >= 1024;
   switch (epi) {
-    case EPI_BF16: return launch_cfg<128, 128, 2, 2, EPI_BF16>(a, s);
-    case EPI_F32: return launch_cfg<128, 128, 2, 2, EPI_F32>(a, s);
-    case EPI_RESID: return launch_cfg<128, 128, 2, 2, EPI_RESID>(a, s);
-    case EPI_SWIGLU: return launch_cfg<128, 64, 2, 2, EPI_SWIGLU>(a, s);
+    case EPI_BF16:
+      return big ? launch_cfg<256, 256, 4, 2, 64, 2, EPI_BF16>(a, s) : launch_cfg<128, 128, 2, 2, 64, 2, EPI_BF16>(a, s);
+    case EPI_F32: return launch_cfg<128, 128, 2, 2, 64, 2, EPI_F32>(a, s);
+    case EPI_RESID: return launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);
+    case EPI_SWIGLU:
+      return big ? launch_cfg<256, 128, 4, 2, 64, 2, EPI_SWIGLU>(a, s) : launch_cfg<128, 64, 2, 2, 64, 2, EPI_SWIGLU>(a, s);
   }
   return (int)hipErrorInvalidValue;
 }

@@ -25,7 +25,7 @@ def _rel(a, b):
 
 
 SHAPES = [(34, 128, 64), (300, 176, 64), (129, 257, 176), (1, 64, 4096), (4160, 384, 512),
-          (64, 1000, 4096)]
+          (64, 1000, 4096), (1040, 2056, 520), (700, 1300, 200), (512, 1024, 64)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -58,7 +58,7 @@ def test_gemm_epilogues(M, N, K, epi):
     assert _rel(got, ref) < tol
 
 
-@pytest.mark.parametrize("M,F,K", [(34, 176, 64), (257, 200, 128), (1024, 1024, 512)])
+@pytest.mark.parametrize("M,F,K", [(34, 176, 64), (257, 200, 128), (1024, 1024, 512), (777, 1160, 264)])
 def test_gemm_swiglu(M, F, K):
     print(f"swiglu M={M} F={F} K={K}", flush=True)
     rng = np.random.default_rng(M + F)
