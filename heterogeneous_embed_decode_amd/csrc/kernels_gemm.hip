@@ -28,6 +28,9 @@ struct GemmArgs {
   const uint16_t *U;
   const uint16_t *Bx;
   int ldu, r, lrows, sec1, sec2;
+  // stream-K (residual epilogue only): 0 = one workgroup per output tile;
+  // otherwise the number of workgroups sharing the tile x K-step space
+  int sk_grid;
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -83,32 +86,29 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  // tile order: XCD-contiguous ranges, then groups of GM tile rows walked
-  // column by column so that resident workgroups share B tiles in L2
+  // tile order: groups of GM tile rows walked column by column so that
+  // resident workgroups share B tiles in L2
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + BN - 1) / BN;
   const int P = tiles_m * tiles_n;
-  int pid = blockIdx.x;
-  {
-    const int per = P / 8;
-    if (pid < per * 8) pid = (pid % 8) * per + pid / 8;
-  }
   constexpr int GM = 16;
-  const int group = pid / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gsz = min(tiles_m - first_m, GM);
-  const int within = pid % (GM * tiles_n);
-  const int tm = first_m + within % gsz;
-  const int tn = within / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
+  int m0 = 0, n0 = 0;
+  auto set_tile = [&](int t) {
+    const int group = t / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    const int within = t % (GM * tiles_n);
+    m0 = (first_m + within % gsz) * BM;
+    n0 = (within / gsz) * BN;
+  };
+  // hardware places workgroup b on XCD b % 8: give each XCD a contiguous
+  // range of logical indices so its L2 sees neighbouring tiles
+  auto xcd_remap = [](int b, int n) {
+    const int per = n / 8;
+    return b < per * 8 ? (b % 8) * per + b / 8 : b;
+  };
 
   f32x16_t acc[MI][NI];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // B tile row rr -> output column of that row and its global B row
   auto b_src_row = [&](int rr, int &ncol) -> int {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   };
 
   // phase 0: main operands over K; phase 1: adapter operands over ldu
-  auto run_phase = [&](const int phase, const int Kp) {
+  auto run_phase = [&](const int phase, const int Kp, const int kb, const int ke) {
     const uint16_t *abase = phase == 0 ? g.A : g.U;
     const int alda = phase == 0 ? g.lda : g.ldu;
     const int arows = phase == 0 ? g.M : min(g.M, g.lrows);
@@ -224,69 +224,111 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
             rb, (lds_ptr_t)(Bs0 + st * BNB * BK + (i * NW + wave) * 512), 16, off, 0, 0, 0);
       }
     };
-    const int nk = (Kp + BK - 1) / BK;
-    // S-stage ring: tiles kt+1 .. kt+S-2 stay in flight while tile kt is
-    // consumed; one barrier per tile both publishes tile kt and retires
-    // the stage that the next issue overwrites.  The bare s_barrier avoids
-    // the fence of __syncthreads, which would drain the loads in flight.
+    // S-stage ring over K-steps [kb, ke): steps kt+1 .. kt+S-2 stay in
+    // flight while step kt is consumed; one barrier per step both publishes
+    // step kt and retires the stage that the next issue overwrites.  The
+    // bare s_barrier avoids the fence of __syncthreads, which would drain
+    // the loads in flight.
 #pragma unroll
     for (int p = 0; p < S - 1; ++p)
-      if (p < nk) issue(p);
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_tiles<LPT, S>(min(S - 2, nk - 1 - kt));
+      if (kb + p < ke) issue(kb + p);
+    for (int kt = kb; kt < ke; ++kt) {
+      wait_tiles<LPT, S>(min(S - 2, ke - 1 - kt));
       __builtin_amdgcn_s_barrier();
-      if (kt + S - 1 < nk) issue(kt + S - 1);
+      if (kt + S - 1 < ke) issue(kt + S - 1);
       compute(kt % S);
     }
   };
 
-  run_phase(0, g.K);
-  if (!DUAL && g.U != nullptr && m0 < g.lrows) {
-    __builtin_amdgcn_s_barrier();  // all waves are done with the last stage
-    run_phase(1, g.ldu);
-  }
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  };
 
+  const int nk = (g.K + BK - 1) / BK;
+  const bool lora_tile_possible = !DUAL && g.U != nullptr;
   // epilogue: lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane/32) + e%4
-  const int jc = lane & 31;
-  const int rbase = (lane >> 5) * 4;
+  auto epilogue = [&](const bool atomic) {
+    const int jc = lane & 31;
+    const int rbase = (lane >> 5) * 4;
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    if (DUAL) {
+    for (int i = 0; i < MI; ++i) {
+      if (DUAL) {
 #pragma unroll
-      for (int j = 0; j < NI / 2; ++j) {
-        const int n = n0 + wn * WCN + j * 32 + jc;
-        if (n >= g.N) continue;
+        for (int j = 0; j < NI / 2; ++j) {
+          const int n = n0 + wn * WCN + j * 32 + jc;
+          if (n >= g.N) continue;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
-          if (m >= g.M) continue;
-          const float gt = acc[i][j][e], up = acc[i][j + NI / 2][e];
-          const float sg = gt / (1.f + expf(-gt));
-          ((uint16_t *)g.C)[(size_t)m * g.ldc + n] = (uint16_t)f2bf(sg * up);
+          for (int e = 0; e < 16; ++e) {
+            const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
+            if (m >= g.M) continue;
+            const float gt = acc[i][j][e], up = acc[i][j + NI / 2][e];
+            const float sg = gt / (1.f + expf(-gt));
+            ((uint16_t *)g.C)[(size_t)m * g.ldc + n] = (uint16_t)f2bf(sg * up);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int n = n0 + wn * WCN + j * 32 + jc;
+          if (n >= g.N) continue;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
+            if (m >= g.M) continue;
+            const size_t o = (size_t)m * g.ldc + n;
+            const float v = acc[i][j][e];
+            if (EPI == EPI_BF16) ((uint16_t *)g.C)[o] = (uint16_t)f2bf(g.alpha * v);
+            else if (EPI == EPI_F32) ((float *)g.C)[o] = g.alpha * v;
+            else if (atomic) unsafeAtomicAdd((float *)g.C + o, v);
+            else ((float *)g.C)[o] += v;
+          }
         }
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int n = n0 + wn * WCN + j * 32 + jc;
-        if (n >= g.N) continue;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
-          if (m >= g.M) continue;
-          const size_t o = (size_t)m * g.ldc + n;
-          const float v = acc[i][j][e];
-          if (EPI == EPI_BF16) ((uint16_t *)g.C)[o] = (uint16_t)f2bf(g.alpha * v);
-          else if (EPI == EPI_F32) ((float *)g.C)[o] = g.alpha * v;
-          else ((float *)g.C)[o] += v;
-        }
+    }
+  };
+
+  if (g.sk_grid == 0) {
+    set_tile(xcd_remap(blockIdx.x, P));
+    zero_acc();
+    run_phase(0, g.K, 0, nk);
+    if (lora_tile_possible && m0 < g.lrows) {
+      __builtin_amdgcn_s_barrier();  // all waves are done with the last stage
+      run_phase(1, g.ldu, 0, (g.ldu + BK - 1) / BK);
+    }
+    epilogue(false);
+  } else if (EPI == EPI_RESID) {
+    // stream-K: equal shares of the P x nk iteration space; partial tiles
+    // are added into the fp32 residual with hardware float atomics (the
+    // summation order of the partials is therefore not fixed)
+    const long total = (long)P * nk;
+    const int w = xcd_remap(blockIdx.x, g.sk_grid);
+    long it = total * w / g.sk_grid;
+    const long it_end = total * (w + 1) / g.sk_grid;
+    while (it < it_end) {
+      const int t = (int)(it / nk);
+      const int kb = (int)(it % nk);
+      const int ke = (int)min((long)nk, kb + (it_end - it));
+      set_tile(t);
+      zero_acc();
+      __builtin_amdgcn_s_barrier();  // previous segment's stages are retired
+      run_phase(0, g.K, kb, ke);
+      if (ke == nk && lora_tile_possible && m0 < g.lrows) {
+        __builtin_amdgcn_s_barrier();
+        run_phase(1, g.ldu, 0, (g.ldu + BK - 1) / BK);
       }
+      epilogue(true);
+      it += ke - kb;
     }
   }
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int S, int EPI>
-static int launch_cfg(const GemmArgs &a, hipStream_t s) {
+static int launch_cfg(GemmArgs a, hipStream_t s, int sk_grid = 0) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (tiles == 0) return 0;
   constexpr int BNB = (EPI == EPI_SWIGLU) ? 2 * BN : BN;
@@ -298,9 +340,21 @@ static int launch_cfg(const GemmArgs &a, hipStream_t s) {
     if (e != hipSuccess) return (int)e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(WM * WN * 64), lds, s, a);
+  a.sk_grid = sk_grid;
+  hipLaunchKernelGGL(kern, dim3(sk_grid > 0 ? sk_grid : tiles), dim3(WM * WN * 64), lds, s, a);
   ORTHRUS_LAUNCH_CHECK();
   return 0;
+}
+
+static int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
 }
 
 int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C, int ldc, int M,
@@ -317,15 +371,18 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
   }
   hipStream_t s = (hipStream_t)stream;
   // Tile shapes measured on MI355X for the decoder's projections: 256-row
-  // tiles on 8 waves (two per SIMD) for wide outputs; 128x128 on 4 waves for
-  // the residual projections (more tiles, better balance over 256 CUs) and
-  // for small problems.
+  // tiles on 8 waves (two per SIMD) for large problems, 128x128 on 4 waves
+  // for small ones.
   const bool big = M >= 512 && N >= 1024;
   switch (epi) {
     case EPI_BF16:
       return big ? launch_cfg<256, 256, 4, 2, 64, 2, EPI_BF16>(a, s) : launch_cfg<128, 128, 2, 2, 64, 2, EPI_BF16>(a, s);
     case EPI_F32: return launch_cfg<128, 128, 2, 2, 64, 2, EPI_F32>(a, s);
-    case EPI_RESID: return launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);
+    case EPI_RESID:
+      // residual projections have few output tiles (N = d): stream-K over
+      // one workgroup per CU keeps every CU busy to the end
+      return big ? launch_cfg<256, 256, 4, 2, 64, 2, EPI_RESID>(a, s, cu_count())
+                 : launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);
     case EPI_SWIGLU:
       return big ? launch_cfg<256, 128, 4, 2, 64, 2, EPI_SWIGLU>(a, s) : launch_cfg<128, 64, 2, 2, 64, 2, EPI_SWIGLU>(a, s);
   }

@@ -25,7 +25,8 @@ def _rel(a, b):
 
 
 SHAPES = [(34, 128, 64), (300, 176, 64), (129, 257, 176), (1, 64, 4096), (4160, 384, 512),
-          (64, 1000, 4096), (1040, 2056, 520), (700, 1300, 200), (512, 1024, 64)]
+          (64, 1000, 4096), (1040, 2056, 520), (700, 1300, 200), (512, 1024, 64),
+          (2000, 1536, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
