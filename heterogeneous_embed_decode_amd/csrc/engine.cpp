@@ -313,8 +313,8 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
     eng->part_ml = eng->part_o = nullptr;
     eng->part_cap = 0;
     const int Gq = c.n_q_heads / c.n_kv_heads;
-    if (hipMalloc(&eng->part_ml, cap * ATTN_WAVES * Gq * 2 * 4) != hipSuccess ||
-        hipMalloc(&eng->part_o, cap * ATTN_WAVES * Gq * (size_t)c.head_dim * 4) != hipSuccess) {
+    if (hipMalloc(&eng->part_ml, cap * Gq * 2 * 4) != hipSuccess ||
+        hipMalloc(&eng->part_o, cap * Gq * (size_t)c.head_dim * 4) != hipSuccess) {
       eng->err = "partial buffer allocation failed";
       return ORTHRUS_ENOMEM;
     }

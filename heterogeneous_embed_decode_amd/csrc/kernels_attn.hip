@@ -15,11 +15,13 @@
 //           formed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMAs with K
 //           staged in LDS; P^T stays in registers and O^T = V^T P^T reads a
 //           transposed V tile from LDS.  Online softmax in fp32 (exp2).
-//  DECODE : one decode row, one KV head, up to 256 keys; each wave walks
-//           64 keys with HD/8 lanes per key so every page (page_size x HD
-//           contiguous bf16) is read with 16-byte coalesced loads, serving
-//           all grouped query heads from one read; it writes (max, sum,
-//           unnormalised output) for the combine.
+//  DECODE : one decode row, one KV head, up to 128 keys; each wave issues
+//           all K and V loads of its 32 keys at once (HD/8 lanes per key,
+//           16-byte loads over the contiguous page_size x HD blocks) and
+//           serves all grouped query heads from one read; the four waves
+//           merge in LDS and write one (max, sum, unnormalised output)
+//           partial, or the finished output when one split covers the whole
+//           context.
 #include "device_common.h"
 #include "orthrus_internal.h"
 
@@ -39,7 +41,7 @@ struct AttnArgs {
   float scale_log2;
 };
 
-constexpr int KT = 64;  // keys per chunk-path tile
+constexpr int KT = 32;  // keys per chunk-path tile
 
 template <int HD>
 struct ChunkSmem {
@@ -195,33 +197,62 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
     }
 }
 
+// DPP helpers: sums over the 2/4/8/16 lanes of one key within a 16-lane
+// row without going through the LDS crossbar.  quad_perm [1,0,3,2] and
+// [2,3,0,1] exchange lanes 1 and 2 apart; row_half_mirror pairs lane i with
+// 7-i (the other quad of the half-row); row_mirror pairs i with 15-i (the
+// other half of the row).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+template <int LPK>
+__device__ __forceinline__ float key_sum(float v) {
+  if (LPK >= 2) v += dpp<0xB1>(v);
+  if (LPK >= 4) v += dpp<0x4E>(v);
+  if (LPK >= 8) v += dpp<0x141>(v);
+  if (LPK >= 16) v += dpp<0x140>(v);
+  return v;
+}
+
 template <int HD, int G>
-__device__ void decode_path(const AttnArgs &a, const AttnWork &w) {
-  constexpr int LPK = HD / 8;              // lanes per key
-  constexpr int KPI = 64 / LPK;            // keys per load instruction
-  constexpr int NLD = KPI >= 16 ? 1 : 16 / KPI;
-  constexpr int BLK = KPI * NLD;           // keys per softmax block
-  constexpr int WSPAN = ATTN_SPLIT / ATTN_WAVES;
+struct DecodeSmem {
+  float o[ATTN_WAVES][G * HD];
+  float ml[ATTN_WAVES][G][2];
+  int pages[ATTN_SPLIT + 2];
+};
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+// q_pair . k_pair in fp32 (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2(uint32_t q2, uint32_t k2, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q2), __builtin_bit_cast(bf16x2_t, k2), c,
+                                         false);
+}
+
+// Decode work: keys [k0, k1) (at most 128) of one decode row and one KV
+// head.  The split's page ids are staged in LDS once.  Each wave takes 32
+// keys and issues all of their K and V loads before any arithmetic (HD/8
+// lanes per key, 16-byte loads over the contiguous page_size x HD blocks),
+// scores all grouped query heads with packed bf16 dot products, and the
+// four waves merge in LDS: one partial per workgroup, or the final output
+// when this split covers the whole context.
+template <int HD, int G>
+__device__ void decode_path(const AttnArgs &a, const AttnWork &w, DecodeSmem<HD, G> &sm) {
+  constexpr int LPK = HD / 8;                  // lanes per key
+  constexpr int KPI = 64 / LPK;                // keys per wave load
+  constexpr int WK = ATTN_SPLIT / ATTN_WAVES;  // keys per wave
+  constexpr int NL = WK / KPI > 0 ? WK / KPI : 1;
+  static_assert(NL * KPI >= WK, "wave key span");
   const DevItem it = a.items[w.item];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPK, kg = lane / LPK;
-  const int wk0 = w.k0 + wave * WSPAN;
-  const int wk1 = min(w.k1, wk0 + WSPAN);
-  const int32_t *pages = a.page_ids + it.page_off;
-
-  float q[G][8];
-  {
-    const uint16_t *qrow = a.qkv + (size_t)it.row0 * a.ld_qkv + (w.kvh * G) * HD + sub * 8;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const u32x4_t v = *(const u32x4_t *)(qrow + h * HD);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        q[h][2 * e] = lo_bf(v[e]) * a.scale_log2;
-        q[h][2 * e + 1] = hi_bf(v[e]) * a.scale_log2;
-      }
-    }
-  }
+  const int pi0 = w.k0 / a.ps;
+  const int npg = (w.k1 - 1) / a.ps - pi0 + 1;
+  for (int t = threadIdx.x; t < npg; t += 256) sm.pages[t] = a.page_ids[it.page_off + pi0 + t];
+  __syncthreads();
+  const int wk0 = w.k0 + wave * WK;
+  const int wk1 = min(w.k1, wk0 + WK);
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -230,65 +261,58 @@ __device__ void decode_path(const AttnArgs &a, const AttnWork &w) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  for (int kb = wk0; kb < wk1; kb += BLK) {
-    float sc[NLD][G];
-    u32x4_t vv[NLD];
+  if (wk0 < wk1) {
+    // all loads first; lanes past the end re-read the last key (masked)
+    u32x4_t kr[NL], vr[NL];
+    const size_t head_off = (size_t)w.kvh * a.ps;
 #pragma unroll
-    for (int li = 0; li < NLD; ++li) {
-      const int key = kb + li * KPI + kg;
-      const bool valid = key < wk1;
-      u32x4_t kv = {0u, 0u, 0u, 0u};
-      vv[li] = kv;
-      if (valid) {
-        const int page = pages[key / a.ps];
-        const size_t off = (((size_t)page * a.Hkv + w.kvh) * a.ps + key % a.ps) * HD + sub * 8;
-        kv = *(const u32x4_t *)(a.kc + off);
-        vv[li] = *(const u32x4_t *)(a.vc + off);
-      }
-      float kf[8];
+    for (int li = 0; li < NL; ++li) {
+      const int key = min(wk0 + li * KPI + kg, wk1 - 1);
+      const int page = sm.pages[key / a.ps - pi0];
+      const size_t off = (((size_t)page * a.Hkv * a.ps) + head_off + key % a.ps) * HD + sub * 8;
+      kr[li] = *(const u32x4_t *)(a.kc + off);
+      vr[li] = *(const u32x4_t *)(a.vc + off);
+    }
+    u32x4_t q[G];
+    const uint16_t *qrow = a.qkv + (size_t)it.row0 * a.ld_qkv + (w.kvh * G) * HD + sub * 8;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = lo_bf(kv[e]);
-        kf[2 * e + 1] = hi_bf(kv[e]);
-      }
+    for (int h = 0; h < G; ++h) q[h] = *(const u32x4_t *)(qrow + h * HD);
+    float sc[NL][G];
+#pragma unroll
+    for (int li = 0; li < NL; ++li) {
+      const bool valid = wk0 + li * KPI + kg < wk1;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(q[h][e], kf[e], d);
-#pragma unroll
-        for (int o = 1; o < LPK; o <<= 1) d += __shfl_xor(d, o, 64);
+        float d = dot2(q[h][0], kr[li][0], 0.f);
+        d = dot2(q[h][1], kr[li][1], d);
+        d = dot2(q[h][2], kr[li][2], d);
+        d = dot2(q[h][3], kr[li][3], d);
+        d = key_sum<LPK>(d) * a.scale_log2;
         sc[li][h] = valid ? d : -INFINITY;
       }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mb = sc[0][h];
+      float mx = sc[0][h];
 #pragma unroll
-      for (int li = 1; li < NLD; ++li) mb = fmaxf(mb, sc[li][h]);
+      for (int li = 1; li < NL; ++li) mx = fmaxf(mx, sc[li][h]);
 #pragma unroll
-      for (int o = LPK; o < 64; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o, 64));
-      const float m_new = fmaxf(m[h], mb);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m[h] - m_use);
-      m[h] = m_new;
-      l[h] *= alpha;
+      for (int o = LPK; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      m[h] = mx;  // finite: the wave has at least one valid key
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-#pragma unroll
-      for (int li = 0; li < NLD; ++li) {
-        const float p = exp2f(sc[li][h] - m_use);
-        l[h] += p;
+      for (int li = 0; li < NL; ++li) {
+        const float pr = exp2f(sc[li][h] - mx);
+        l[h] += pr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[h][2 * e] = fmaf(p, lo_bf(vv[li][e]), acc[h][2 * e]);
-          acc[h][2 * e + 1] = fmaf(p, hi_bf(vv[li][e]), acc[h][2 * e + 1]);
+          acc[h][2 * e] = fmaf(pr, lo_bf(vr[li][e]), acc[h][2 * e]);
+          acc[h][2 * e + 1] = fmaf(pr, hi_bf(vr[li][e]), acc[h][2 * e + 1]);
         }
       }
     }
   }
-  // sum the key groups (each LPK-lane group saw different keys)
-  const int pidx = w.part * ATTN_WAVES + wave;
+  // sum the key groups (each LPK-lane group saw different keys) and stage
+  // this wave's (m, l, o) in LDS
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float lt = l[h];
@@ -302,47 +326,124 @@ __device__ void decode_path(const AttnArgs &a, const AttnWork &w) {
       acc[h][e] = v;
     }
     if (kg == 0) {
-      float *dst = a.part_o + ((size_t)pidx * G + h) * HD + sub * 8;
+      float *dst = &sm.o[wave][h * HD + sub * 8];
       *(float4 *)dst = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
       *(float4 *)(dst + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
     }
     if (lane == 0) {
-      a.part_ml[((size_t)pidx * G + h) * 2 + 0] = m[h];
-      a.part_ml[((size_t)pidx * G + h) * 2 + 1] = lt;
+      sm.ml[wave][h][0] = m[h];
+      sm.ml[wave][h][1] = lt;
+    }
+  }
+  __syncthreads();
+  const bool whole = (w.k0 == 0 && w.k1 == it.ctx + 1);
+  for (int t = threadIdx.x; t < G * HD; t += 256) {
+    const int h = t / HD, d = t % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < ATTN_WAVES; ++v) M = fmaxf(M, sm.ml[v][h][0]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int v = 0; v < ATTN_WAVES; ++v) {
+      if (sm.ml[v][h][0] == -INFINITY) continue;  // a wave with no keys
+      const float wgt = exp2f(sm.ml[v][h][0] - M);
+      L += wgt * sm.ml[v][h][1];
+      O += wgt * sm.o[v][t];
+    }
+    if (whole) {
+      a.o[(size_t)it.row0 * a.ld_o + (w.kvh * G + h) * HD + d] = (uint16_t)f2bf(O / L);
+    } else {
+      a.part_o[((size_t)w.part * G + h) * HD + d] = O;
+      if (d == 0) {
+        a.part_ml[((size_t)w.part * G + h) * 2 + 0] = M;
+        a.part_ml[((size_t)w.part * G + h) * 2 + 1] = L;
+      }
     }
   }
 }
 
 template <int HD, int G>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) ChunkSmem<HD> sm;
+__global__ __launch_bounds__(256, 3) void attention_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) union {
+    ChunkSmem<HD> c;
+    DecodeSmem<HD, G> d;
+  } sm;
   const AttnWork w = a.work[blockIdx.x];
-  if (w.type == WORK_CHUNK) chunk_path<HD>(a, w, sm);
-  else decode_path<HD, G>(a, w);
+  if (w.type == WORK_CHUNK) chunk_path<HD>(a, w, sm.c);
+  else decode_path<HD, G>(a, w, sm.d);
 }
 
-// Merge the split partials of each decode row: out = sum_p exp2(m_p - M) o_p /
-// sum_p exp2(m_p - M) l_p.  Grid (decode item, query head), HD threads.
+// Merge the split partials of each decode row: out = sum_p 2^(m_p - M) o_p /
+// sum_p 2^(m_p - M) l_p.  Grid (decode item, KV head), 256 threads.  The
+// per-partial weights of every grouped head are formed once into LDS
+// (lanes over partials), then each thread sums its output elements over
+// the partials with independent coalesced loads.  Rows whose context fits
+// one split were finished by the attention kernel itself.
+constexpr int COMB_MAXP = 256;  // partials merged per pass
+
 template <int HD>
-__global__ void attn_combine_kernel(const DevItem *items, const int32_t *dec_items, const float *part_ml,
-                                    const float *part_o, uint16_t *o, int ld_o, int G) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(const DevItem *items, const int32_t *dec_items,
+                                                           const float *part_ml, const float *part_o,
+                                                           uint16_t *o, int ld_o, int G) {
+  __shared__ float wts[8][COMB_MAXP];
+  __shared__ float Ms[8], Mrun[8], Lrun[8];
   const DevItem it = items[dec_items[blockIdx.x]];
-  const int h = blockIdx.y;
-  const int kvh = h / G, hh = h % G;
-  const int d = threadIdx.x;
-  const int p0 = (it.part0 + kvh * it.n_parts) * ATTN_WAVES;
-  const int np = it.n_parts * ATTN_WAVES;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, part_ml[((size_t)(p0 + p) * G + hh) * 2]);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, acc = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const size_t idx = (size_t)(p0 + p) * G + hh;
-    const float wgt = exp2f(part_ml[idx * 2] - Mu);
-    L += wgt * part_ml[idx * 2 + 1];
-    acc += wgt * part_o[idx * HD + d];
+  if (it.n_parts <= 1) return;
+  const int kvh = blockIdx.y;
+  const int p0 = it.part0 + kvh * it.n_parts;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int PER = (8 * HD + 255) / 256;  // output elements per thread (G <= 8)
+  float accs[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) accs[i] = 0.f;
+  if (threadIdx.x < 8) {
+    Mrun[threadIdx.x] = -INFINITY;
+    Lrun[threadIdx.x] = 0.f;
   }
-  o[(size_t)it.row0 * ld_o + h * HD + d] = (uint16_t)f2bf(acc / L);
+  for (int q0 = 0; q0 < it.n_parts; q0 += COMB_MAXP) {
+    const int np = min(COMB_MAXP, it.n_parts - q0);
+    __syncthreads();
+    // weights of this pass, one wave per head
+    for (int h = wave; h < G; h += 4) {
+      float M = -INFINITY;
+      for (int p = lane; p < np; p += 64) M = fmaxf(M, part_ml[((size_t)(p0 + q0 + p) * G + h) * 2]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+      const float Mnew = fmaxf(M, Mrun[h]);
+      float L = 0.f;
+      for (int p = lane; p < np; p += 64) {
+        const size_t idx = (size_t)(p0 + q0 + p) * G + h;
+        const float wgt = exp2f(part_ml[idx * 2] - Mnew);
+        wts[h][p] = wgt;
+        L += wgt * part_ml[idx * 2 + 1];
+      }
+      L = wave_sum(L);
+      if (lane == 0) {
+        Ms[h] = exp2f(Mrun[h] - Mnew);  // rescale of the earlier passes
+        Lrun[h] = Lrun[h] * Ms[h] + L;
+        Mrun[h] = Mnew;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int t = threadIdx.x + i * 256;
+      if (t >= G * HD) break;
+      const int h = t / HD, d = t % HD;
+      float a = accs[i] * Ms[h];
+      const float *src = part_o + (size_t)(p0 + q0) * G * HD + h * HD + d;
+      for (int p = 0; p < np; ++p) a = fmaf(wts[h][p], src[(size_t)p * G * HD], a);
+      accs[i] = a;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int t = threadIdx.x + i * 256;
+    if (t >= G * HD) break;
+    const int h = t / HD, d = t % HD;
+    o[(size_t)it.row0 * ld_o + (kvh * G + h) * HD + d] = (uint16_t)f2bf(accs[i] / Lrun[h]);
+  }
 }
 
 template <int HD>
@@ -385,12 +486,12 @@ int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_de
   if (n_dec <= 0) return 0;
   const int G = Hq / Hkv;
   hipStream_t s = (hipStream_t)stream;
-  dim3 grid(n_dec, Hq);
+  dim3 grid(n_dec, Hkv);
   switch (hd) {
-    case 16: hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(16), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
-    case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, grid, dim3(32), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
-    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, grid, dim3(64), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
-    case 128: hipLaunchKernelGGL(attn_combine_kernel<128>, grid, dim3(128), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
+    case 16: hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(256), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
+    case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, grid, dim3(256), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
+    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, grid, dim3(256), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
+    case 128: hipLaunchKernelGGL(attn_combine_kernel<128>, grid, dim3(256), 0, s, items, dec_items, part_ml, part_o, o, ld_o, G); break;
     default: return (int)hipErrorInvalidValue;
   }
   ORTHRUS_LAUNCH_CHECK();

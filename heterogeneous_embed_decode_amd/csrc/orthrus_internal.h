@@ -23,7 +23,7 @@ orthrus_status validate_and_pack(const orthrus_model_cfg &cfg, const orthrus_bat
 //  CHUNK : rows [q0, q0+qn) of item `item` (local row indices) for KV head
 //          `kvh`, against keys [0, ctx + q0 + qn).
 //  DECODE: the decode row of `item` for KV head `kvh` against keys
-//          [k0, k1); each of the 4 waves writes partial `part*4 + wave`.
+//          [k0, k1); the workgroup writes partial `part`.
 enum { WORK_CHUNK = 0, WORK_DECODE = 1 };
 struct AttnWork {
   int32_t type, item, kvh, q0, qn, k0, k1, part;
@@ -34,7 +34,7 @@ struct DevItem {
 };
 
 constexpr int ATTN_ROWS = 128;       // (token, head) rows per chunk workgroup
-constexpr int ATTN_SPLIT = 256;      // keys per decode workgroup (64 per wave)
+constexpr int ATTN_SPLIT = 128;      // keys per decode workgroup (32 per wave)
 constexpr int ATTN_WAVES = 4;
 
 void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const HostPack &p,
