@@ -23,6 +23,7 @@ struct orthrus_engine {
   // workspace
   float *x = nullptr;
   uint16_t *h = nullptr, *qkv = nullptr, *o = nullptr, *act = nullptr, *U = nullptr;
+  float *U32 = nullptr;  // adapter shrink accumulator, zero between uses
   float *hf = nullptr;
   uint16_t *hl = nullptr;
   double *inv_freq = nullptr;
@@ -151,7 +152,7 @@ static void free_all(orthrus_engine *e) {
   e->marks.clear();
   for (auto ev : e->ev_free) (void)hipEventDestroy(ev);
   e->ev_free.clear();
-  void *ptrs[] = {e->x, e->h, e->qkv, e->o, e->act, e->U, e->hf, e->hl, e->inv_freq,
+  void *ptrs[] = {e->x, e->h, e->qkv, e->o, e->act, e->U, e->U32, e->hf, e->hl, e->inv_freq,
                   e->part_ml, e->part_o, e->meta_dev};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
@@ -173,7 +174,8 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
   if (c.n_q_heads % c.n_kv_heads) return ORTHRUS_EINVAL;
   const int G = c.n_q_heads / c.n_kv_heads;
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) return ORTHRUS_EINVAL;
-  if (c.d_model % 8 || c.ffn_dim % 8 || c.lora_rank % 8) return ORTHRUS_EINVAL;
+  if (c.d_model % 8 || c.ffn_dim % 8 || c.lora_rank % 8 || c.d_model > 8192 || c.lora_rank > 64)
+    return ORTHRUS_EINVAL;
   for (int l = 0; l < c.n_layers; ++l) {
     const orthrus_layer_w &L = w->layers[l];
     if (!L.w_qkv || !L.w_o || !L.w_gate_up || !L.w_down || !L.g_attn || !L.g_ffn) return ORTHRUS_EINVAL;
@@ -207,12 +209,14 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
       {(void **)&eng->o, T * qd * 2},
       {(void **)&eng->act, T * (size_t)c.ffn_dim * 2},
       {(void **)&eng->U, T * (size_t)std::max(3 * c.lora_rank, 8) * 2},
+      {(void **)&eng->U32, T * (size_t)std::max(3 * c.lora_rank, 8) * 4},
       {(void **)&eng->hf, T * d * 4},
       {(void **)&eng->hl, T * d * 2},
       {(void **)&eng->inv_freq, (size_t)hd / 2 * 8},
   };
   for (auto &a : allocs)
     if (hipMalloc(a.p, a.bytes) != hipSuccess) return bail(ORTHRUS_ENOMEM);
+  if (hipMemset(eng->U32, 0, T * (size_t)std::max(3 * c.lora_rank, 8) * 4) != hipSuccess) return bail(ORTHRUS_EHIP);
   std::vector<double> inv(hd / 2);
   for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / hd);
   if (hipMemcpy(eng->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice) != hipSuccess)
@@ -346,16 +350,20 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   const int TE = p.rows_by_kind[0];
   const size_t layer_kv = (size_t)c.n_pages * Hkv * c.page_size * hd;
 
-  LCHK(launch_embed_gather(d_tok, (const uint16_t *)eng->w.tok_emb, eng->x, T, d, s), "embed_gather");
   for (int l = 0; l < c.n_layers; ++l) {
     const orthrus_layer_w &L = eng->layers[l];
     uint16_t *kc = eng->kc + (size_t)l * layer_kv, *vc = eng->vc + (size_t)l * layer_kv;
     const bool lora = r > 0 && TE > 0;
-    LCHK(launch_rmsnorm(eng->x, (const uint16_t *)L.g_attn, eng->h, T, d, c.rms_eps, s), "rmsnorm");
+    if (l == 0)
+      LCHK(launch_embed_rmsnorm(d_tok, (const uint16_t *)eng->w.tok_emb, (const uint16_t *)L.g_attn, eng->x,
+                                eng->h, T, d, c.rms_eps, s),
+           "embed_rmsnorm");
+    else
+      LCHK(launch_rmsnorm(eng->x, (const uint16_t *)L.g_attn, eng->h, T, d, c.rms_eps, s), "rmsnorm");
     LoraArgs la{};
     if (lora) {
-      LCHK(launch_gemm(eng->h, d, (const uint16_t *)L.lora_a_qkv, d, eng->U, 3 * r, TE, 3 * r, d, EPI_BF16, 0,
-                       c.lora_scale, nullptr, s),
+      LCHK(launch_lora_shrink(eng->h, d, (const uint16_t *)L.lora_a_qkv, TE, 3 * r, d, c.lora_scale, eng->U32,
+                              eng->U, s),
            "lora_shrink_qkv");
       la.U = eng->U; la.ldu = 3 * r; la.Bx = (const uint16_t *)L.lora_b_qkv; la.r = r; la.rows = TE;
       la.sec1 = qd; la.sec2 = qd + kvd;
@@ -372,8 +380,8 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
                              Hq, Hkv, hd, s),
          "attn_combine");
     if (lora) {
-      LCHK(launch_gemm(eng->o, qd, (const uint16_t *)L.lora_a_o, qd, eng->U, r, TE, r, qd, EPI_BF16, 0,
-                       c.lora_scale, nullptr, s),
+      LCHK(launch_lora_shrink(eng->o, qd, (const uint16_t *)L.lora_a_o, TE, r, qd, c.lora_scale, eng->U32, eng->U,
+                              s),
            "lora_shrink_o");
       la.ldu = r; la.Bx = (const uint16_t *)L.lora_b_o; la.sec1 = d; la.sec2 = d;
     }

@@ -13,29 +13,60 @@
 
 namespace orthrus {
 
-// x[t, :] = fp32(E[tok[t], :]); one workgroup per row, 8 values per chunk.
-__global__ void embed_gather_kernel(const int32_t *tok, const uint16_t *E, float *x, int d) {
-  const int t = blockIdx.x;
-  const uint16_t *src = E + (size_t)tok[t] * d;
-  float *dst = x + (size_t)t * d;
-  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
-    const u32x4_t w = *(const u32x4_t *)(src + c * 8);
-    float4 a = make_float4(lo_bf(w[0]), hi_bf(w[0]), lo_bf(w[1]), hi_bf(w[1]));
-    float4 b = make_float4(lo_bf(w[2]), hi_bf(w[2]), lo_bf(w[3]), hi_bf(w[3]));
-    *(float4 *)(dst + c * 8) = a;
-    *(float4 *)(dst + c * 8 + 4) = b;
-  }
-}
-
 __device__ __forceinline__ float block_sum_256(float v, float *red) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
   float s = 0.f;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s += red[i];
   __syncthreads();
   return s;
+}
+
+// Rows of up to NORM_MAXV * 1024 values are held in registers (float4 per
+// thread and slot) between the sum of squares and the scaled write-out, so
+// x is read from HBM once.
+constexpr int NORM_MAXV = 8;
+
+__device__ __forceinline__ void norm_write_bf16(const float4 *v, const uint16_t *g, uint16_t *hr, int nv4,
+                                                float inv) {
+#pragma unroll
+  for (int j = 0; j < NORM_MAXV; ++j) {
+    const int c = threadIdx.x + j * 256;
+    if (c >= nv4) break;
+    const uint2 gw = *(const uint2 *)(g + c * 4);
+    uint2 o;
+    o.x = pack_bf2(v[j].x * inv * lo_bf(gw.x), v[j].y * inv * hi_bf(gw.x));
+    o.y = pack_bf2(v[j].z * inv * lo_bf(gw.y), v[j].w * inv * hi_bf(gw.y));
+    *(uint2 *)(hr + c * 4) = o;
+  }
+}
+
+// x[t] = fp32(E[tok[t]]) and h[t] = bf16(rmsnorm(x[t]) * g): the embedding
+// gather fused with the first layer's attention norm.
+__global__ __launch_bounds__(256) void embed_rmsnorm_kernel(const int32_t *tok, const uint16_t *E,
+                                                            const uint16_t *g, float *x, uint16_t *h, int d,
+                                                            float eps) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const uint16_t *src = E + (size_t)tok[t] * d;
+  float *xr = x + (size_t)t * d;
+  const int nv4 = d / 4;
+  float4 v[NORM_MAXV];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NORM_MAXV; ++j) {
+    const int c = threadIdx.x + j * 256;
+    if (c >= nv4) break;
+    const uint2 w = *(const uint2 *)(src + c * 4);
+    v[j] = make_float4(lo_bf(w.x), hi_bf(w.x), lo_bf(w.y), hi_bf(w.y));
+    *(float4 *)(xr + c * 4) = v[j];
+    ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  }
+  ss = block_sum_256(ss, red);
+  norm_write_bf16(v, g, h + (size_t)t * d, nv4, 1.f / sqrtf(ss / (float)d + eps));
 }
 
 // h[row] = bf16(x[row] / sqrt(mean(x[row]^2) + eps) * g); 256 threads per row.
@@ -44,62 +75,69 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, const uint
   __shared__ float red[4];
   const int t = blockIdx.x;
   const float *xr = x + (size_t)t * d;
+  const int nv4 = d / 4;
+  float4 v[NORM_MAXV];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d / 4; c += blockDim.x) {
-    const float4 v = *(const float4 *)(xr + c * 4);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int j = 0; j < NORM_MAXV; ++j) {
+    const int c = threadIdx.x + j * 256;
+    if (c >= nv4) break;
+    v[j] = *(const float4 *)(xr + c * 4);
+    ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
   }
   ss = block_sum_256(ss, red);
-  const float inv = 1.f / sqrtf(ss / (float)d + eps);
-  uint16_t *hr = h + (size_t)t * d;
-  for (int c = threadIdx.x; c < d / 4; c += blockDim.x) {
-    const float4 v = *(const float4 *)(xr + c * 4);
-    const uint2 gw = *(const uint2 *)(g + c * 4);
-    uint2 o;
-    o.x = pack_bf2(v.x * inv * lo_bf(gw.x), v.y * inv * hi_bf(gw.x));
-    o.y = pack_bf2(v.z * inv * lo_bf(gw.y), v.w * inv * hi_bf(gw.y));
-    *(uint2 *)(hr + c * 4) = o;
-  }
+  norm_write_bf16(v, g, h + (size_t)t * d, nv4, 1.f / sqrtf(ss / (float)d + eps));
 }
 
 // Rotate-half RoPE on q (in place) and k, then append k and v of every row
-// at its KV slot.  Angles pos * inv_freq[i] are formed in fp64.
+// at its KV slot.  The row's angles pos * inv_freq[i] are formed in fp64
+// once (cos/sin staged in LDS); each thread then rotates 8 consecutive
+// pairs with 16-byte loads and stores.
 // Cache layout: [page][kv_head][slot_in_page][head_dim].
 __global__ __launch_bounds__(256) void rope_kv_kernel(uint16_t *qkv, const int32_t *pos,
                                                       const int32_t *slot, const double *inv_freq,
                                                       uint16_t *kc, uint16_t *vc, int Hq, int Hkv,
                                                       int hd, int ps) {
+  __shared__ float cs[64], sn[64];
   const int t = blockIdx.x;
   const int half = hd / 2;
+  if ((int)threadIdx.x < half) {
+    const double ang = (double)pos[t] * inv_freq[threadIdx.x];
+    cs[threadIdx.x] = (float)cos(ang);
+    sn[threadIdx.x] = (float)sin(ang);
+  }
+  __syncthreads();
   const int ld = (Hq + 2 * Hkv) * hd;
   uint16_t *row = qkv + (size_t)t * ld;
-  const double p = (double)pos[t];
   const int s = slot[t];
   const int page = s / ps, off = s % ps;
-  // q and k heads: one (head, pair) per thread iteration
-  const int n_rot = (Hq + Hkv) * half;
-  for (int w = threadIdx.x; w < n_rot; w += blockDim.x) {
-    const int head = w / half, i = w % half;
-    const double ang = p * inv_freq[i];
-    const float c = (float)cos(ang), sn = (float)sin(ang);
+  const int gph = half / 8;  // groups of 8 pairs per head
+  for (int w = threadIdx.x; w < (Hq + Hkv) * gph; w += blockDim.x) {
+    const int head = w / gph, i0 = (w % gph) * 8;
     uint16_t *base = row + head * hd;
-    const float x1 = bf2f(base[i]), x2 = bf2f(base[i + half]);
-    const uint16_t o1 = (uint16_t)f2bf(x1 * c - x2 * sn);
-    const uint16_t o2 = (uint16_t)f2bf(x2 * c + x1 * sn);
+    const u32x4_t a = *(const u32x4_t *)(base + i0);
+    const u32x4_t b = *(const u32x4_t *)(base + half + i0);
+    u32x4_t oa, ob;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + 2 * e;
+      const float a0 = lo_bf(a[e]), a1 = hi_bf(a[e]), b0 = lo_bf(b[e]), b1 = hi_bf(b[e]);
+      oa[e] = pack_bf2(a0 * cs[i] - b0 * sn[i], a1 * cs[i + 1] - b1 * sn[i + 1]);
+      ob[e] = pack_bf2(b0 * cs[i] + a0 * sn[i], b1 * cs[i + 1] + a1 * sn[i + 1]);
+    }
     if (head < Hq) {
-      base[i] = o1;
-      base[i + half] = o2;
+      *(u32x4_t *)(base + i0) = oa;
+      *(u32x4_t *)(base + half + i0) = ob;
     } else {
-      const int g = head - Hq;
-      uint16_t *dst = kc + (((size_t)page * Hkv + g) * ps + off) * hd;
-      dst[i] = o1;
-      dst[i + half] = o2;
+      uint16_t *dst = kc + (((size_t)page * Hkv + (head - Hq)) * ps + off) * hd;
+      *(u32x4_t *)(dst + i0) = oa;
+      *(u32x4_t *)(dst + half + i0) = ob;
     }
   }
   const uint16_t *vsrc = row + (Hq + Hkv) * hd;
-  for (int w = threadIdx.x; w < Hkv * hd; w += blockDim.x) {
-    const int g = w / hd, e = w % hd;
-    vc[(((size_t)page * Hkv + g) * ps + off) * hd + e] = vsrc[w];
+  for (int w = threadIdx.x; w < Hkv * hd / 8; w += blockDim.x) {
+    const int g = (w * 8) / hd, e = (w * 8) % hd;
+    *(u32x4_t *)(vc + (((size_t)page * Hkv + g) * ps + off) * hd + e) = *(const u32x4_t *)(vsrc + w * 8);
   }
 }
 
@@ -114,26 +152,30 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float *x, const u
   const bool emb = b < n_embed;
   const int row = emb ? b : logit_rows[b - n_embed];
   const float *xr = x + (size_t)row * d;
+  const int nv4 = d / 4;
+  float4 v[NORM_MAXV];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d / 4; c += blockDim.x) {
-    const float4 v = *(const float4 *)(xr + c * 4);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int j = 0; j < NORM_MAXV; ++j) {
+    const int c = threadIdx.x + j * 256;
+    if (c >= nv4) break;
+    v[j] = *(const float4 *)(xr + c * 4);
+    ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
   }
   ss = block_sum_256(ss, red);
   const float inv = 1.f / sqrtf(ss / (float)d + eps);
-  for (int c = threadIdx.x; c < d / 4; c += blockDim.x) {
-    const float4 v = *(const float4 *)(xr + c * 4);
+  if (!emb) {
+    norm_write_bf16(v, g, hl + (size_t)(b - n_embed) * d, nv4, inv);
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < NORM_MAXV; ++j) {
+    const int c = threadIdx.x + j * 256;
+    if (c >= nv4) break;
     const uint2 gw = *(const uint2 *)(g + c * 4);
-    const float4 o = make_float4(v.x * inv * lo_bf(gw.x), v.y * inv * hi_bf(gw.x),
-                                 v.z * inv * lo_bf(gw.y), v.w * inv * hi_bf(gw.y));
-    if (emb) {
-      *(float4 *)(hf + (size_t)b * d + c * 4) = o;
-    } else {
-      uint2 w;
-      w.x = pack_bf2(o.x, o.y);
-      w.y = pack_bf2(o.z, o.w);
-      *(uint2 *)(hl + (size_t)(b - n_embed) * d + c * 4) = w;
-    }
+    *(float4 *)(hf + (size_t)b * d + c * 4) =
+        make_float4(v[j].x * inv * lo_bf(gw.x), v[j].y * inv * hi_bf(gw.x), v[j].z * inv * lo_bf(gw.y),
+                    v[j].w * inv * hi_bf(gw.y));
   }
 }
 
@@ -192,9 +234,10 @@ __global__ void pool_wsum_kernel(const int32_t *segs, int n_segs, float *wsum) {
   wsum[slot] = (first ? 0.f : wsum[slot]) + (float)add;
 }
 
-int launch_embed_gather(const int32_t *tok, const uint16_t *E, float *x, int T, int d, void *stream) {
+int launch_embed_rmsnorm(const int32_t *tok, const uint16_t *E, const uint16_t *g, float *x, uint16_t *h, int T,
+                         int d, float eps, void *stream) {
   if (T <= 0) return 0;
-  hipLaunchKernelGGL(embed_gather_kernel, dim3(T), dim3(256), 0, (hipStream_t)stream, tok, E, x, d);
+  hipLaunchKernelGGL(embed_rmsnorm_kernel, dim3(T), dim3(256), 0, (hipStream_t)stream, tok, E, g, x, h, d, eps);
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }
@@ -232,6 +275,97 @@ int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, fl
   ORTHRUS_LAUNCH_CHECK();
   hipLaunchKernelGGL(pool_wsum_kernel, dim3((n_segs + 63) / 64), dim3(64), 0, (hipStream_t)stream, segs,
                      n_segs, wsum);
+  ORTHRUS_LAUNCH_CHECK();
+  return 0;
+}
+
+}  // namespace orthrus
+
+namespace orthrus {
+
+// Adapter shrink, U32[m, j] += sum_{k in split} X[m, k] A[j, k] for m < rows,
+// j < nr (the LoRA "A" projection of the embedding rows; Efficient
+// Iterative Retrieval with Heterogeneous Batching, §2.2 Parameter sharing).
+// Grid (row blocks of 32, K splits), 4 waves: each wave covers a quarter of
+// the block's K range with 32x32x16 bf16 MFMAs on operands read straight
+// from global memory; the waves reduce in LDS and the block adds its
+// partial into U32 with float atomics.  nr <= 64 * LS_NB.
+constexpr int LS_NB = 6;  // up to 192 adapter columns (3 x rank 64)
+
+__global__ __launch_bounds__(256) void lora_shrink_kernel(const uint16_t *X, int ldx, const uint16_t *A, int rows,
+                                                          int nr, int K, int ksplit, float *U32) {
+  extern __shared__ float red_dyn[];  // [4 waves][nb][16][64]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const int m0 = blockIdx.x * 32;
+  const int kper = ((K + ksplit - 1) / ksplit + 63) / 64 * 64;
+  const int kb = blockIdx.y * kper, ke = min(K, kb + kper);
+  const int nb = (nr + 31) / 32;
+  f32x16_t acc[LS_NB];
+#pragma unroll
+  for (int j = 0; j < LS_NB; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+  const int row = m0 + (lane & 31);
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+  for (int k = kb + wave * 16; k < ke; k += 64) {
+    const int kk = k + half * 8;
+    const bool kin = kk < ke;
+    const u32x4_t a = (row < rows && kin) ? *(const u32x4_t *)(X + (size_t)row * ldx + kk) : zero4;
+#pragma unroll
+    for (int j = 0; j < LS_NB; ++j) {
+      if (j >= nb) break;
+      const int col = j * 32 + (lane & 31);
+      const u32x4_t b = (col < nr && kin) ? *(const u32x4_t *)(A + (size_t)col * K + kk) : zero4;
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, b), acc[j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < LS_NB; ++j) {
+    if (j >= nb) break;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red_dyn[((wave * nb + j) * 16 + e) * 64 + lane] = acc[j][e];
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < nb * 16 * 64; t += 256) {
+    const int j = t / 1024, e = (t / 64) % 16, l = t % 64;
+    const int q = (j * 16 + e) * 64 + l, st = nb * 16 * 64;
+    const float v = red_dyn[q] + red_dyn[st + q] + red_dyn[2 * st + q] + red_dyn[3 * st + q];
+    const int m = m0 + (e / 4) * 8 + (l >> 5) * 4 + (e % 4);
+    const int col = j * 32 + (l & 31);
+    if (m < rows && col < nr) unsafeAtomicAdd(U32 + (size_t)m * nr + col, v);
+  }
+}
+
+// U[m, j] = bf16(scale * U32[m, j]); U32 is cleared for its next use.
+__global__ void lora_convert_kernel(float *U32, uint16_t *U, int n, float scale) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  U[i] = (uint16_t)f2bf(scale * U32[i]);
+  U32[i] = 0.f;
+}
+
+int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, int nr, int K, float scale,
+                       float *U32, uint16_t *U, void *stream) {
+  if (rows <= 0 || nr <= 0) return 0;
+  if (nr > 32 * LS_NB) return (int)hipErrorInvalidValue;
+  hipStream_t s = (hipStream_t)stream;
+  const int rb = (rows + 31) / 32;
+  int ksplit = 1;
+  while (rb * ksplit < 512 && K / (ksplit * 2) >= 256) ksplit *= 2;
+  const int nb = (nr + 31) / 32;
+  const size_t lds = (size_t)4 * nb * 16 * 64 * sizeof(float);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)lora_shrink_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(4 * LS_NB * 16 * 64 * sizeof(float)));
+    if (e != hipSuccess) return (int)e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(lora_shrink_kernel, dim3(rb, ksplit), dim3(256), lds, s, X, ldx, A, rows, nr, K, ksplit, U32);
+  ORTHRUS_LAUNCH_CHECK();
+  const int n = rows * nr;
+  hipLaunchKernelGGL(lora_convert_kernel, dim3((n + 255) / 256), dim3(256), 0, s, U32, U, n, scale);
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }

@@ -56,8 +56,8 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
                 int M, int N, int K, int epi, int b_up_row, float alpha,
                 const LoraArgs *lora, void *stream);
 
-int launch_embed_gather(const int32_t *tok, const uint16_t *E, float *x, int T, int d,
-                        void *stream);
+int launch_embed_rmsnorm(const int32_t *tok, const uint16_t *E, const uint16_t *g, float *x, uint16_t *h,
+                         int T, int d, float eps, void *stream);
 int launch_rmsnorm(const float *x, const uint16_t *g, uint16_t *h, int T, int d, float eps,
                    void *stream);
 int launch_rope_kv(uint16_t *qkv, const int32_t *pos, const int32_t *slot,
@@ -72,6 +72,8 @@ int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_de
                         int Hq, int Hkv, int hd, void *stream);
 int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_rows, int n_embed,
                       int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream);
+int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, int nr, int K, float scale,
+                       float *U32, uint16_t *U, void *stream);
 int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, float *wsum,
                 float *kept, float *emb, int d, void *stream);
 

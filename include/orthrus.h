@@ -149,7 +149,8 @@ orthrus_status orthrus_pack(const orthrus_model_cfg *cfg, const orthrus_batch *b
  * weight pointer table; allocates the workspace for max_tokens/max_items.
  * k_pages / v_pages: device bf16 KV pools (layout above), read and written
  * by every step.  Returns EINVAL for unsupported shapes (head_dim not in
- * {16,32,64,128}, n_q_heads not a multiple of n_kv_heads, d_model, Hq*hd,
+ * {16,32,64,128}, n_q_heads not a multiple of n_kv_heads, d_model above
+ * 8192, d_model, Hq*hd,
  * ffn_dim not multiples of 8, lora_rank not a multiple of 8), ENOMEM or
  * EHIP on allocation failure. */
 orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weights *w,
