@@ -73,16 +73,20 @@ def kernel_source_digest():
 def traffic_from_profiles(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}_one_layer_traffic.json")
+    p = os.path.join(ROOT, "profiles", f"{kernel}_one_layer_traffic.md")
     if not os.path.exists(p):
         return None
-    try:
-        rec = json.load(open(p))
-    except Exception:
-        return None
+    rec = {}
+    for line in open(p):
+        if ":" in line and not line.startswith(("|", "#", " ", "`")):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
     if rec.get("kernel_source_sha256_16") != kernel_source_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, batch, n_pages, bits, kv_bits):
@@ -107,6 +111,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of 1 GiB (read) into 1 GiB (write), 5 times; "
+                         "used to scale the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the step needs no collective and each replica is "
@@ -115,6 +122,16 @@ def main():
 
     import numpy as np
     import torch
+    if args.copy_calibration:
+        n = 1 << 28  # float32 elements: 1 GiB
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                          "launches": 5}), flush=True)
+        return
     import heterogeneous_embed_decode_amd as hed
     from heterogeneous_embed_decode_amd.device_model import DeviceModel
     from synth import model as sm

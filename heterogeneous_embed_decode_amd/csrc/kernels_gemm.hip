@@ -31,6 +31,7 @@ struct GemmArgs {
   // stream-K (residual epilogue only): 0 = one workgroup per output tile;
   // otherwise the number of workgroups sharing the tile x K-step space
   int sk_grid;
+  int group_m;  // tile rows per group of the tile order (0 = default)
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -54,7 +55,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // wait until at most `tiles_after` tiles of LPT loads per lane are in flight
 template <int LPT, int S>
 __device__ __forceinline__ void wait_tiles(int tiles_after) {
-  if (S >= 4 && tiles_after >= 2) wait_vmcnt<(S >= 4 ? 2 : 0) * LPT>();
+  if (S >= 5 && tiles_after >= 3) wait_vmcnt<(S >= 5 ? 3 : 0) * LPT>();
+  else if (S >= 4 && tiles_after >= 2) wait_vmcnt<(S >= 4 ? 2 : 0) * LPT>();
   else if (S >= 3 && tiles_after >= 1) wait_vmcnt<(S >= 3 ? 1 : 0) * LPT>();
   else wait_vmcnt<0>();
 }
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int B_ROUNDS = BNB / (RPI * NW);
   constexpr int LPT = A_ROUNDS + B_ROUNDS;      // loads per lane per tile
   static_assert(A_ROUNDS * RPI * NW == BM && B_ROUNDS * RPI * NW == BNB, "tile/threads mismatch");
-  static_assert(S >= 2 && S <= 4, "2..4 stages");
+  static_assert(S >= 2 && S <= 5, "2..5 stages");
 
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t *const As0 = smem;                   // [S][BM * BK]
@@ -86,12 +88,13 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  // tile order: groups of GM tile rows walked column by column so that
-  // resident workgroups share B tiles in L2
+  // tile order: groups of GM tile rows walked column by column, so the ~32
+  // workgroups resident on one XCD cover about 4 x 8 tiles and share both
+  // A and B tiles in that XCD's L2 (measured best at GM = 4)
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + BN - 1) / BN;
   const int P = tiles_m * tiles_n;
-  constexpr int GM = 16;
+  const int GM = g.group_m > 0 ? g.group_m : 4;
   int m0 = 0, n0 = 0;
   auto set_tile = [&](int t) {
     const int group = t / (GM * tiles_n);
@@ -371,20 +374,29 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
   }
   hipStream_t s = (hipStream_t)stream;
   // Tile shapes measured on MI355X for the decoder's projections: 256-row
-  // tiles on 8 waves (two per SIMD) for large problems, 128x128 on 4 waves
-  // for small ones.
+  // tiles on 8 waves (two per SIMD) for large problems; a 64-row tile with a
+  // 4-deep load ring for few rows (LM head, decode-only batches), where the
+  // weights stream from HBM; 128x128 on 4 waves otherwise.
   const bool big = M >= 512 && N >= 1024;
+  const bool skinny = M <= 64;
   switch (epi) {
     case EPI_BF16:
-      return big ? launch_cfg<256, 256, 4, 2, 64, 2, EPI_BF16>(a, s) : launch_cfg<128, 128, 2, 2, 64, 2, EPI_BF16>(a, s);
-    case EPI_F32: return launch_cfg<128, 128, 2, 2, 64, 2, EPI_F32>(a, s);
+      if (big) return launch_cfg<256, 256, 2, 4, 64, 2, EPI_BF16>(a, s);
+      if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_BF16>(a, s);
+      return launch_cfg<128, 128, 2, 2, 64, 2, EPI_BF16>(a, s);
+    case EPI_F32:
+      if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_F32>(a, s);
+      return launch_cfg<128, 128, 2, 2, 64, 2, EPI_F32>(a, s);
     case EPI_RESID:
       // residual projections have few output tiles (N = d): stream-K over
       // one workgroup per CU keeps every CU busy to the end
-      return big ? launch_cfg<256, 256, 4, 2, 64, 2, EPI_RESID>(a, s, cu_count())
-                 : launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);
+      if (big) return launch_cfg<256, 256, 4, 2, 64, 2, EPI_RESID>(a, s, cu_count());
+      if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_RESID>(a, s);
+      return launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);
     case EPI_SWIGLU:
-      return big ? launch_cfg<256, 128, 4, 2, 64, 2, EPI_SWIGLU>(a, s) : launch_cfg<128, 64, 2, 2, 64, 2, EPI_SWIGLU>(a, s);
+      if (big) return launch_cfg<256, 128, 2, 4, 64, 2, EPI_SWIGLU>(a, s);
+      if (skinny) return launch_cfg<64, 64, 2, 2, 64, 4, EPI_SWIGLU>(a, s);
+      return launch_cfg<128, 64, 2, 2, 64, 2, EPI_SWIGLU>(a, s);
   }
   return (int)hipErrorInvalidValue;
 }
