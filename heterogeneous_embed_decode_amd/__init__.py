@@ -84,6 +84,8 @@ def _load():
     lib.orthrus_destroy.restype = None
     lib.orthrus_gemm_bf16.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.orthrus_gemm_bf16.restype = ctypes.c_int
+    lib.orthrus_fill_hash_bf16.argtypes = [_vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64, _vp]
+    lib.orthrus_fill_hash_bf16.restype = ctypes.c_int
     lib.orthrus_profile.argtypes = [_vp, _i32]
     lib.orthrus_profile.restype = ctypes.c_int
     lib.orthrus_profile_read.argtypes = [_vp, ctypes.c_char_p, _i32]
@@ -93,7 +95,8 @@ def _load():
 
 LIB = _load()
 EXPORTS = ("orthrus_pack", "orthrus_create", "orthrus_step", "orthrus_last_error",
-           "orthrus_destroy", "orthrus_gemm_bf16", "orthrus_profile", "orthrus_profile_read")
+           "orthrus_destroy", "orthrus_gemm_bf16", "orthrus_profile", "orthrus_profile_read",
+           "orthrus_fill_hash_bf16")
 
 
 class OrthrusError(RuntimeError):
@@ -198,3 +201,7 @@ def orthrus_profile_read(eng) -> dict:
     buf = ctypes.create_string_buffer(n + 1)
     LIB.orthrus_profile_read(eng, buf, n + 1)
     return json.loads(buf.value.decode())
+
+
+def orthrus_fill_hash_bf16(dst, n, seed, tensor_id, start=0, stream=None) -> int:
+    return LIB.orthrus_fill_hash_bf16(dst, n, seed, tensor_id, start, stream)

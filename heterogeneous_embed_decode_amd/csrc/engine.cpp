@@ -461,6 +461,12 @@ int32_t orthrus_profile_read(orthrus_engine *eng, char *json, int32_t len) {
   return (int32_t)out.size();
 }
 
+orthrus_status orthrus_fill_hash_bf16(void *dst, uint64_t n, uint32_t seed, uint32_t tensor_id, uint64_t start,
+                                     void *stream) {
+  if (!dst && n) return ORTHRUS_EINVAL;
+  return launch_hash_fill((uint16_t *)dst, n, seed, tensor_id, start, stream) ? ORTHRUS_EHIP : ORTHRUS_OK;
+}
+
 orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int32_t ldb, void *C, int32_t ldc,
                                  int32_t M, int32_t N, int32_t K, int32_t epilogue, int32_t b_up_row,
                                  void *stream) {

@@ -371,3 +371,35 @@ int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, 
 }
 
 }  // namespace orthrus
+
+namespace orthrus {
+
+// Seeded synthetic bf16 values from the SplitMix64 counter hash (Steele,
+// Lea and Flood 2014): value i of (seed, tensor_id) is
+//   z = ((seed << 32) ^ tensor_id) + (i + 1) * 0x9E3779B97F4A7C15
+//   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9; z = (z ^ (z >> 27)) * 0x94D049BB133111EB
+//   h = z ^ (z >> 31); u = (h >> 40) * 2^-24; v = bf16_rne((2u - 1) * 1.7320508f)
+// Every step is exact integer arithmetic or one correctly rounded fp32
+// operation, so any implementation of the definition gives the same bits.
+__global__ void hash_fill_kernel(uint16_t *dst, uint64_t n, uint64_t key, uint64_t start) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    uint64_t z = key + (start + i + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z = z ^ (z >> 31);
+    const float u = (float)(uint32_t)(z >> 40) * (1.0f / 16777216.0f);
+    const float t = 2.0f * u - 1.0f;   // exact
+    dst[i] = (uint16_t)f2bf(__fmul_rn(t, 1.7320508f));
+  }
+}
+
+int launch_hash_fill(uint16_t *dst, uint64_t n, uint32_t seed, uint32_t tensor_id, uint64_t start, void *stream) {
+  if (n == 0) return 0;
+  const uint64_t key = ((uint64_t)seed << 32) ^ (uint64_t)tensor_id;
+  hipLaunchKernelGGL(hash_fill_kernel, dim3(4096), dim3(256), 0, (hipStream_t)stream, dst, n, key, start);
+  ORTHRUS_LAUNCH_CHECK();
+  return 0;
+}
+
+}  // namespace orthrus

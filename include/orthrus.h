@@ -193,6 +193,18 @@ void orthrus_destroy(orthrus_engine *eng);
 orthrus_status orthrus_profile(orthrus_engine *eng, int32_t enable);
 int32_t orthrus_profile_read(orthrus_engine *eng, char *json, int32_t len);
 
+/* Seeded synthetic bf16 fill (device): dst[i] = value start+i of the
+ * SplitMix64 counter hash keyed by (seed, tensor_id), mapped to a uniform
+ * value of unit variance and rounded to bf16:
+ *   z = ((seed << 32) ^ tensor_id) + (start + i + 1) * 0x9E3779B97F4A7C15
+ *   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9; z = (z ^ (z >> 27)) * 0x94D049BB133111EB
+ *   h = z ^ (z >> 31); u = (h >> 40) * 2^-24; v = bf16_rne((2u - 1) * 1.7320508f)
+ * Used to lay down prior KV pages and other synthetic state of large
+ * workloads without a host upload; the definition is exact, so a host
+ * implementation reproduces the same bits.  Asynchronous on `stream`. */
+orthrus_status orthrus_fill_hash_bf16(void *dst, uint64_t n, uint32_t seed, uint32_t tensor_id, uint64_t start,
+                                      void *stream);
+
 /* Standalone bf16 GEMM on the MFMA kernels of the step (device pointers):
  *   C = A B^T with A [M][K] (lda), B [N][K] (ldb), fp32 accumulation.
  * epilogue: 0 store C as bf16 [M][N] (ldc); 1 store fp32; 2 fp32 C += A B^T;

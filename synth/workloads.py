@@ -263,3 +263,163 @@ def synthetic_kv(cfg: ModelConfig, n_pages: int, seed: int = 3):
     k = normal_bf16([seed, 0], n, 1.0).reshape(shape)
     v = normal_bf16([seed, 1], n, 1.0).reshape(shape)
     return k, v
+
+
+# ---- the three large workloads ----------------------------------------------
+# Prior state of a workload: every KV page of every layer holds SplitMix64
+# values (seed KV_SEED, tensor 0 for K and 1 for V) over the linear index of
+# the [layer][page][kv_head][slot][head_dim] pool; pooling slots hold
+# SplitMix64 values (tensor 2 for the running sum, 3 for the kept state) over
+# slot * d + j, and a weight total equal to the closed form of the tokens
+# before the chunk (c for mean, c(c+1)/2 for weighted mean).
+KV_SEED = 3
+POOL_SUM_TID, POOL_KEPT_TID = 2, 3
+
+
+@dataclass
+class Workload:
+    cfg: ModelConfig
+    batches: List[Batch]
+    n_pages: int
+    n_slots: int
+    prior_wsum: Dict[int, float] = field(default_factory=dict)   # slot -> weight total before step 0
+
+
+def _prior_total(kind: int, c: int) -> float:
+    if kind == POOL_MEAN:
+        return float(c)
+    if kind == POOL_WMEAN:
+        return float(c * (c + 1) // 2)
+    return 0.0
+
+
+def _budget_batch(cfg, rng_tok, bb, emb_entries, dec_ids):
+    return bb.build(emb_entries + [(rid, DECODE, 1, 0, 1) for rid in dec_ids])
+
+
+def nine_to_one_workload(n_layers: int = 32, steps: int = 10, budget: int = 8192, chunk: int = 256,
+                         seed_len: int = 2, seed_tok: int = 1, n_decode: int = 819,
+                         cfg: ModelConfig = None) -> Workload:
+    """Mistral-7B shape at a 9:1 embedding:generation token mix: 819 decode
+    rows (contexts uniform in [500, 3500], +1 per step) and embedding
+    requests of U[256, 4096] tokens in chunks of 256 with mean pooling,
+    admitted first come first served into the remaining budget of 8192
+    tokens (at most one chunk per request per step; a chunk is admitted only
+    when it fits), for `steps` consecutive steps with pooling state and KV
+    carried between steps.  LoRA rank 16."""
+    cfg = (cfg or MISTRAL_7B).with_(n_layers=n_layers, lora_rank=16)
+    rl = np.random.default_rng(seed_len)
+    rt = np.random.default_rng(seed_tok)
+    ps = cfg.page_size
+    ctxs = rl.integers(500, 3501, n_decode)
+    emb_lens = list(rl.integers(256, 4097, 400))
+    dec_pages = int(sum(-(-(int(c) + steps) // ps) for c in ctxs))
+    emb_pages = (budget // chunk + 2) * (-(-(steps * chunk) // ps)) + 64
+    n_pages = dec_pages + emb_pages
+    alloc = PageAllocator(n_pages, seed=4)
+    bb = BatchBuilder(cfg, alloc)
+    dec_ids = []
+    for j, c in enumerate(ctxs):
+        rid = 100000 + j
+        req = bb.add(Request(rid, DECODE, list(rt.integers(0, cfg.vocab, int(c) + steps + 1))))
+        req.done = int(c)
+        dec_ids.append(rid)
+    n_slots = budget // chunk + 2
+    free_slots = collections.deque(range(n_slots))
+    queue = collections.deque(range(len(emb_lens)))
+    active = []  # request ids in arrival order
+    lens = {}
+    batches = []
+    for _ in range(steps):
+        room = budget - len(dec_ids)
+        entries = []
+        # active requests first (arrival order), then admit new ones
+        for rid in list(active):
+            n = lens[rid]
+            done = bb.reqs[rid].done
+            c = min(chunk, n - done)
+            if c <= room:
+                entries.append((rid, EMBED, c, done == 0, done + c == n))
+                room -= c
+        while queue and room >= min(chunk, emb_lens[queue[0]]) and free_slots:
+            i = queue.popleft()
+            rid = i
+            n = int(emb_lens[i])
+            lens[rid] = n
+            bb.add(Request(rid, EMBED, list(rt.integers(0, cfg.vocab, n)), pool_slot=free_slots.popleft(),
+                           pool_kind=POOL_MEAN))
+            active.append(rid)
+            c = min(chunk, n)
+            entries.append((rid, EMBED, c, True, c == n))
+            room -= c
+        b = _budget_batch(cfg, rt, bb, entries, dec_ids)
+        batches.append(b)
+        bb.commit(b)
+        for it in b.items:
+            if it.kind == EMBED and it.is_last:
+                active.remove(it.req_id)
+                free_slots.append(bb.reqs[it.req_id].pool_slot)
+    return Workload(cfg, batches, n_pages, n_slots)
+
+
+def five_to_five_workload(n_layers: int = 32, seed_len: int = 2, seed_tok: int = 1,
+                          cfg: ModelConfig = None) -> Workload:
+    """Mistral-7B shape at a 5:5 mix, LoRA rank 64: four embedding requests of
+    4096 tokens at chunk indices 0..3 of a 1024 chunking with position-
+    weighted mean pooling (the later chunks carry synthetic prior state),
+    seven 500-token prompt prefill chunks and 596 decode rows with contexts
+    uniform in [500, 3500]: 8192 rows."""
+    cfg = (cfg or MISTRAL_7B).with_(n_layers=n_layers, lora_rank=64)
+    rl = np.random.default_rng(seed_len)
+    rt = np.random.default_rng(seed_tok)
+    ps = cfg.page_size
+    ctxs = rl.integers(500, 3501, 596)
+    n_pages = 4 * (4096 // ps) + 7 * (-(-500 // ps)) + int(sum(-(-(int(c) + 1) // ps) for c in ctxs)) + 16
+    alloc = PageAllocator(n_pages, seed=4)
+    bb = BatchBuilder(cfg, alloc)
+    entries, prior = [], {}
+    for i in range(4):
+        req = bb.add(Request(i, EMBED, list(rt.integers(0, cfg.vocab, 4096)), pool_slot=i, pool_kind=POOL_WMEAN))
+        req.done = i * 1024
+        prior[i] = _prior_total(POOL_WMEAN, req.done)
+        entries.append((i, EMBED, 1024, i == 0, i == 3))
+    for k in range(7):
+        bb.add(Request(1000 + k, PREFILL, list(rt.integers(0, cfg.vocab, 500))))
+        entries.append((1000 + k, PREFILL, 500, True, True))
+    for j, c in enumerate(ctxs):
+        req = bb.add(Request(100000 + j, DECODE, list(rt.integers(0, cfg.vocab, int(c) + 1))))
+        req.done = int(c)
+        entries.append((100000 + j, DECODE, 1, 0, 1))
+    return Workload(cfg, [bb.build(entries)], n_pages, 4, prior)
+
+
+def one_to_nine_workload(n_layers: int = 32, budget: int = 8192, seed_len: int = 2, seed_tok: int = 1,
+                         cfg: ModelConfig = None) -> Workload:
+    """Llama-3.1-8B shape at a decode-heavy 1:9 request mix: 256 decode rows
+    with contexts uniform in [500, 3500] reserved first, then embedding
+    requests of n_docs ~ U{1..10} x 512 tokens with CLS pooling in chunks of
+    512, each at a uniform chunk index (earlier chunks' KV and kept state
+    synthetic), filling the 8192-token budget: 15 chunks, 7936 rows."""
+    from .model import LLAMA31_8B
+    cfg = (cfg or LLAMA31_8B).with_(n_layers=n_layers, lora_rank=16)
+    rl = np.random.default_rng(seed_len)
+    rt = np.random.default_rng(seed_tok)
+    ps = cfg.page_size
+    ctxs = rl.integers(500, 3501, 256)
+    n_chunks = (budget - 256) // 512
+    docs = rl.integers(1, 11, n_chunks)
+    idxs = [int(rl.integers(0, d)) for d in docs]
+    n_pages = int(sum(-(-(int(c) + 1) // ps) for c in ctxs)) + int(sum(int(d) * 512 // ps for d in docs)) + 16
+    alloc = PageAllocator(n_pages, seed=4)
+    bb = BatchBuilder(cfg, alloc)
+    entries = []
+    for i, (d, k) in enumerate(zip(docs, idxs)):
+        n = int(d) * 512
+        req = bb.add(Request(i, EMBED, list(rt.integers(0, cfg.vocab, n)), pool_slot=i, pool_kind=POOL_CLS))
+        req.done = k * 512
+        entries.append((i, EMBED, 512, k == 0, (k + 1) * 512 == n))
+    for j, c in enumerate(ctxs):
+        req = bb.add(Request(100000 + j, DECODE, list(rt.integers(0, cfg.vocab, int(c) + 1))))
+        req.done = int(c)
+        entries.append((100000 + j, DECODE, 1, 0, 1))
+    return Workload(cfg, [bb.build(entries)], n_pages, n_chunks)

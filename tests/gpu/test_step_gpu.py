@@ -100,3 +100,13 @@ def test_degenerate_batches_and_errors():
                                 4, None, None)
     assert st == hed.ECAPACITY
     dev.close()
+
+
+@pytest.mark.parametrize("seed,tid,start,n", [(3, 0, 0, 100003), (3, 1, 123456789012, 4097), (7, 2, 2**33 + 5, 70000)])
+def test_hash_fill_matches_numpy_definition(seed, tid, start, n):
+    from synth.hashfill import splitmix64_fill
+    out = torch.zeros(n, dtype=torch.int16, device="cuda")
+    assert hed.orthrus_fill_hash_bf16(out.data_ptr(), n, seed, tid, start,
+                                      torch.cuda.current_stream().cuda_stream) == hed.OK
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), splitmix64_fill(seed, tid, n, start))
