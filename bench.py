@@ -89,6 +89,52 @@ def traffic_from_profiles(kernel):
         return None
 
 
+WORKLOAD_TEXT = {
+    "one_layer": "one Mistral-7B-shaped layer, LoRA r16 on embedding rows; 8 embedding chunks x 512 tokens "
+                 "(last-token pooling) + 64 decode rows, KV contexts U[500,3500], page 16",
+    "mix91": "32-layer Mistral-7B shape, 9:1 embed:gen tokens, budget 8192, 819 decode rows (KV U[500,3500]) + "
+             "embedding requests U[256,4096] in chunks of 256 (mean), ten distinct steps, LoRA r16",
+    "mix55": "32-layer Mistral-7B shape, 5:5 mix, budget 8192, LoRA r64: 4 x 1024-token weighted-mean chunks, "
+             "7 x 500-token prefill chunks, 596 decode rows (KV U[500,3500])",
+    "mix19": "32-layer Llama-3.1-8B shape, 1:9 requests, budget 8192: 256 decode rows (KV U[500,3500]) + "
+             "15 CLS chunks of 512 tokens, LoRA r16",
+}
+
+
+def cpu_baseline_one_layer(cfg, batch, n_pages, bits, n_slots, prior_wsum):
+    """The oracle on one full-batch layer of a deep workload (prior KV of the
+    batch's pages regenerated on the host), scaled to the full depth."""
+    import numpy as np
+    import oracle
+    from synth.hashfill import splitmix64_fill
+    from synth.bf16 import bf16_bits_to_f32
+    from synth import workloads as wl
+    from threadpoolctl import threadpool_info
+    c1 = cfg.with_(n_layers=1)
+    keep = {k: v for k, v in bits.items() if not k.startswith("layers.") or k.startswith("layers.0.")}
+    W = oracle.widen_weights(keep, np.float32)
+    used = sorted(set(int(p) for p in batch.page_ids))
+    remap = {p: i for i, p in enumerate(used)}
+    blk = cfg.n_kv_heads * cfg.page_size * cfg.head_dim
+    shape = (cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+    K = np.stack([bf16_bits_to_f32(splitmix64_fill(wl.KV_SEED, 0, blk, p * blk)).reshape(shape) for p in used])
+    V = np.stack([bf16_bits_to_f32(splitmix64_fill(wl.KV_SEED, 1, blk, p * blk)).reshape(shape) for p in used])
+    sub = wl.Batch(batch.items, batch.token_ids, np.asarray([remap[int(p)] for p in batch.page_ids], np.int32))
+    pool = oracle.new_pool(n_slots, cfg.d_model, np.float32)
+    for slot, v in prior_wsum.items():
+        pool["wsum"][slot] = v
+    t0 = time.perf_counter()
+    oracle.step(c1, W, sub, ([K], [V]), pool, np.float32)
+    dt1 = time.perf_counter() - t0
+    # one layer plus the head; the other layers cost the same as the first
+    est = dt1 * cfg.n_layers
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": batch.n_tokens / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full-batch layer of the first step ({batch.n_tokens} rows) through the numpy fp32 "
+                      f"oracle, {dt1:.2f} s, extrapolated to {cfg.n_layers} layers (extrapolated from 1 measured "
+                      f"layer)"}
+
+
 def cpu_baseline(cfg, batch, n_pages, bits, kv_bits):
     import numpy as np
     import oracle
@@ -111,6 +157,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="one_layer", choices=["one_layer", "mix91", "mix55", "mix19"],
+                    help="one_layer (default line): one Mistral-7B-shaped layer, 4160 rows; mix91/mix55/mix19: "
+                         "the 32-layer 9:1 (ten distinct steps), 5:5 (rank 64) and Llama-3.1-8B 1:9 workloads")
+    ap.add_argument("--layers", type=int, default=32, help="depth of the mixed workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB (read) into 1 GiB (write), 5 times; "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -138,28 +188,64 @@ def main():
     from synth import workloads as wl
 
     t_setup = time.time()
-    cfg, batch, n_pages = wl.one_layer_workload()
-    bits = sm.make_weights(cfg, seed=0)
-    kv_bits = wl.synthetic_kv(cfg, n_pages, seed=3)
-    dev = DeviceModel(cfg, bits, n_pages, max_tokens=batch.n_tokens, max_items=batch.n_items,
-                      max_pool_slots=16, kv_bits=kv_bits)
-    st, meta, _ = hed.orthrus_pack(dev.cfg, dev.step_args(batch))
-    assert st == hed.OK
-    bargs = dev.step_args(batch)
+    prior_wsum, n_slots = {}, 16
+    if args.workload == "one_layer":
+        cfg, batch, n_pages = wl.one_layer_workload()
+        batches = [batch]
+        bits = sm.make_weights(cfg, seed=0)
+        kv_bits = wl.synthetic_kv(cfg, n_pages, seed=3)
+    else:
+        build = {"mix91": wl.nine_to_one_workload, "mix55": wl.five_to_five_workload,
+                 "mix19": wl.one_to_nine_workload}[args.workload]
+        w = build(n_layers=args.layers)
+        cfg, batches, n_pages, n_slots, prior_wsum = w.cfg, w.batches, w.n_pages, w.n_slots, w.prior_wsum
+        batch = batches[0]
+        bits = sm.make_weights(cfg, seed=0)
+        kv_bits = None
+    max_t = max(b.n_tokens for b in batches)
+    max_i = max(b.n_items for b in batches)
+    dev = DeviceModel(cfg, bits, n_pages, max_tokens=max_t, max_items=max_i,
+                      max_pool_slots=n_slots, kv_bits=kv_bits)
+    if kv_bits is None:
+        # prior KV and pooling state of the mixed workloads: SplitMix64 values
+        # laid down on the device
+        st0 = torch.cuda.current_stream().cuda_stream
+        assert hed.orthrus_fill_hash_bf16(dev.K.data_ptr(), dev.K.numel(), wl.KV_SEED, 0, 0, st0) == hed.OK
+        assert hed.orthrus_fill_hash_bf16(dev.V.data_ptr(), dev.V.numel(), wl.KV_SEED, 1, 0, st0) == hed.OK
+        tmp = torch.empty(n_slots * cfg.d_model, dtype=torch.int16, device="cuda")
+        for tid, dst in ((wl.POOL_SUM_TID, dev.pool_sum), (wl.POOL_KEPT_TID, dev.pool_kept)):
+            assert hed.orthrus_fill_hash_bf16(tmp.data_ptr(), tmp.numel(), wl.KV_SEED, tid, 0, st0) == hed.OK
+            dst[:n_slots].copy_((tmp.to(torch.int32) << 16).view(torch.float32).view(n_slots, cfg.d_model))
+        for slot, v in prior_wsum.items():
+            dev.pool_wsum[slot] = v
+        torch.cuda.synchronize()
+    metas = []
+    for b in batches:
+        st, m, _ = hed.orthrus_pack(dev.cfg, dev.step_args(b))
+        assert st == hed.OK
+        metas.append(m)
+    meta = metas[0]
+    bargs = [dev.step_args(b) for b in batches]
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
-    print(f"setup {time.time() - t_setup:.1f}s rows={batch.n_tokens} items={batch.n_items}",
-          file=sys.stderr, flush=True)
+    print(f"setup {time.time() - t_setup:.1f}s workload={args.workload} layers={cfg.n_layers} "
+          f"rows={[b.n_tokens for b in batches]} items={batch.n_items}", file=sys.stderr, flush=True)
+
+    rows_done = [0]
 
     def run(k):
-        for _ in range(k):
-            s, _, _ = dev.step(batch, stream=sptr, args=bargs)
+        # cycles through the workload's distinct steps (one for the single-step workloads)
+        for i in range(k):
+            j = i % len(batches)
+            s, _, _ = dev.step(batches[j], stream=sptr, args=bargs[j])
             if s != hed.OK:
                 raise hed.OrthrusError(s, hed.orthrus_last_error(dev.eng))
+            rows_done[0] += batches[j].n_tokens
 
     run(args.warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rows_done[0] = 0
     t0 = time.perf_counter()
     e0.record(stream)
     run(args.steps)
@@ -168,7 +254,7 @@ def main():
     wall = time.perf_counter() - t0
     ev_ms = e0.elapsed_time(e1)
     ms_per_step = 1e3 * wall / args.steps
-    value = batch.n_tokens * args.steps / wall
+    value = rows_done[0] / wall
     print(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, {ev_ms / args.steps:.3f} ms/step events",
           file=sys.stderr, flush=True)
 
@@ -178,7 +264,9 @@ def main():
     torch.cuda.synchronize()
     prof = hed.orthrus_profile_read(dev.eng)
     hed.orthrus_profile(dev.eng, False)
-    work = kernel_work(cfg, batch, meta)
+    # algorithmic work per launch, averaged over the distinct steps that ran
+    works = [kernel_work(cfg, b, m) for b, m in zip(batches, metas)]
+    work = {k: tuple(sum(w_[k][i] for w_ in works) / len(works) for i in range(2)) for k in works[0]}
     kernels = {}
     for name, rec in prof.items():
         avg = rec["total_ms"] / max(rec["count"], 1)
@@ -195,8 +283,10 @@ def main():
         achieved, peak, unit, bound = fl / avg_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
     else:
         achieved, peak, unit, bound = by / avg_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    # the committed counter summary covers the one-layer workload only
+    traffic = traffic_from_profiles(dom) if args.workload == "one_layer" else None
     roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(dom),
+            "frac": round(achieved / peak, 4), "traffic": traffic,
             "algorithmic_per_launch": fl if bound == "mfma" else by, "avg_ms": round(avg_s * 1e3, 5)}
     # decode attention is the HBM-bound part of the path: report its bandwidth too
     if "attention" in prof:
@@ -206,7 +296,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("timing the CPU oracle on the same step ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, batch, n_pages, bits, kv_bits)
+        if args.workload == "one_layer":
+            cpu = cpu_baseline(cfg, batch, n_pages, bits, kv_bits)
+        else:
+            cpu = cpu_baseline_one_layer(cfg, batch, n_pages, bits, n_slots, prior_wsum)
 
     out = {
         "metric": METRIC,
@@ -221,10 +314,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "one Mistral-7B-shaped layer, LoRA r16 on embedding rows; 8 embedding "
-                               "chunks x 512 tokens (last-token pooling) + 64 decode rows, KV contexts "
-                               "U[500,3500], page 16",
-                   "rows": batch.n_tokens, "embed_rows": meta["n_embed_rows"],
+        "config": {"workload": WORKLOAD_TEXT[args.workload],
+                   "rows": batch.n_tokens, "distinct_steps": len(batches), "embed_rows": meta["n_embed_rows"],
                    "decode_rows": meta["n_decode_rows"], "layers": cfg.n_layers, "d_model": cfg.d_model,
                    "ffn_dim": cfg.ffn_dim, "vocab": cfg.vocab, "lora_rank": cfg.lora_rank},
         "roofline": roof,
