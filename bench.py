@@ -49,15 +49,20 @@ def kernel_work(cfg, batch, meta):
         else:
             n, c = it.n_tokens, it.ctx_len
             pairs += n * c + n * (n + 1) // 2
-    attn_flops = 4.0 * hd * cfg.n_q_heads * (pairs + dec_keys)
-    attn_bytes = 2.0 * 2 * kvd * dec_keys
+    # chunk attention: QK^T and PV over the causal pairs; decode attention:
+    # every key of every decode row read once per KV head (K and V, bf16)
+    chunk_flops = 4.0 * hd * cfg.n_q_heads * pairs
+    chunk_bytes = 2.0 * 2 * kvd * sum(it.ctx_len + it.n_tokens for it in batch.items if it.kind != 2)
+    dec_flops = 4.0 * hd * cfg.n_q_heads * dec_keys
+    dec_bytes = 2.0 * 2 * kvd * dec_keys
     return {
         "gemm_qkv": (2.0 * T * qkvd * d + 2.0 * TE * r * qkvd, 2.0 * (T * d + qkvd * d + T * qkvd)),
         "gemm_o": (2.0 * T * d * qd + 2.0 * TE * r * d, 2.0 * (T * qd + d * qd) + 8.0 * T * d),
         "gemm_gate_up": (2.0 * T * 2 * F * d, 2.0 * (T * d + 2 * F * d + T * F)),
         "gemm_down": (2.0 * T * d * F, 2.0 * (T * F + d * F) + 8.0 * T * d),
         "lm_head": (2.0 * G * V * d, 2.0 * (G * d + V * d) + 4.0 * G * V),
-        "attention": (attn_flops, attn_bytes),
+        "attn_chunk": (chunk_flops, chunk_bytes),
+        "attn_decode": (dec_flops, dec_bytes),
         "lora_shrink_qkv": (2.0 * TE * 3 * r * d, 2.0 * (TE * d + 3 * r * d)),
         "lora_shrink_o": (2.0 * TE * r * qd, 2.0 * (TE * qd + r * qd)),
     }
@@ -279,7 +284,7 @@ def main():
     dom = max(prof, key=lambda k: prof[k]["total_ms"])
     fl, by = work.get(dom, (0.0, 0.0))
     avg_s = prof[dom]["total_ms"] / prof[dom]["count"] * 1e-3
-    if dom.startswith("gemm") or dom == "lm_head" and fl / max(by, 1) > 312:
+    if dom.startswith("gemm") or dom == "attn_chunk" or (dom == "lm_head" and fl / max(by, 1) > 312):
         achieved, peak, unit, bound = fl / avg_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
     else:
         achieved, peak, unit, bound = by / avg_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
@@ -289,9 +294,10 @@ def main():
             "frac": round(achieved / peak, 4), "traffic": traffic,
             "algorithmic_per_launch": fl if bound == "mfma" else by, "avg_ms": round(avg_s * 1e3, 5)}
     # decode attention is the HBM-bound part of the path: report its bandwidth too
-    if "attention" in prof:
-        a_avg = prof["attention"]["total_ms"] / prof["attention"]["count"] * 1e-3
-        roof["attention_hbm_gbs"] = round(work["attention"][1] / a_avg / 1e9, 1)
+    if "attn_decode" in prof:
+        a_avg = prof["attn_decode"]["total_ms"] / prof["attn_decode"]["count"] * 1e-3
+        roof["attn_decode_hbm_gbs"] = round(work["attn_decode"][1] / a_avg / 1e9, 1)
+        roof["attn_decode_hbm_frac"] = round(work["attn_decode"][1] / a_avg / 1e9 / PEAK_HBM_GBS, 4)
 
     cpu = None
     if not args.no_cpu_baseline:

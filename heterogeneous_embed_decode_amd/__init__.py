@@ -68,6 +68,15 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python heterogeneous_embed_decode_amd/build.py`")
+    # One HIP runtime per process.  PyTorch's ROCm build ships its own
+    # libamdhip64 (same SONAME, loaded by file name); when it is loaded first
+    # the library's dependency resolves to that copy.  Loaded the other way
+    # round, the process holds two runtimes and the second to initialise
+    # finds no device.  The memory the caller passes comes from PyTorch.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     lib.orthrus_pack.argtypes = [ctypes.POINTER(orthrus_model_cfg), ctypes.POINTER(orthrus_batch),
                                  ctypes.POINTER(orthrus_packed), ctypes.c_char_p, _i32]
@@ -163,7 +172,7 @@ def orthrus_create(cfg: orthrus_model_cfg, tok_emb, lm_head, g_final, layers, k_
     h = _vp()
     st = LIB.orthrus_create(ctypes.byref(cfg), ctypes.byref(w), k_pages, v_pages, ctypes.byref(h))
     if st != OK:
-        raise OrthrusError(st, "orthrus_create failed")
+        raise OrthrusError(st, "orthrus_create failed: " + orthrus_last_error(None))
     return h, (w, arr)
 
 

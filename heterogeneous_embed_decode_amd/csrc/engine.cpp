@@ -97,11 +97,21 @@ size_t align4(size_t n) { return (n + 3) & ~(size_t)3; }
 namespace orthrus {
 
 void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const HostPack &p,
-                     std::vector<AttnWork> &work, std::vector<DevItem> &items, int &n_parts) {
+                     std::vector<AttnWork> &work, std::vector<DevItem> &items, int &n_chunk, int &n_parts) {
   const int G = cfg.n_q_heads / cfg.n_kv_heads;
   const int QB = ATTN_ROWS / G;
   work.clear();
   items.assign(b.n_items, DevItem{});
+  // decode split: the largest allowed size that still yields DEC_MIN_WGS
+  // workgroups (long splits amortise the per-workgroup merge; short ones
+  // fill the chip when there are few decode rows)
+  int split = decode_split_limit(cfg.head_dim);
+  for (; split > DEC_SPLIT_MIN; split /= 2) {
+    long wgs = 0;
+    for (int i = 0; i < b.n_items; ++i)
+      if (b.items[i].kind == ORTHRUS_DECODE) wgs += (b.items[i].ctx_len + split) / split;
+    if (wgs * cfg.n_kv_heads >= DEC_MIN_WGS) break;
+  }
   std::vector<AttnWork> dec;
   n_parts = 0;
   for (int i = 0; i < b.n_items; ++i) {
@@ -120,21 +130,22 @@ void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const
         }
     } else {
       const int nk = it.ctx_len + 1;
-      const int ns = (nk + ATTN_SPLIT - 1) / ATTN_SPLIT;
+      const int ns = (nk + split - 1) / split;
       d.part0 = n_parts;
       d.n_parts = ns;
       for (int g = 0; g < cfg.n_kv_heads; ++g)
         for (int s = 0; s < ns; ++s) {
-          const int k0 = s * ATTN_SPLIT;
-          dec.push_back({WORK_DECODE, i, g, 0, 1, k0, std::min(nk, k0 + ATTN_SPLIT), n_parts + g * ns + s});
+          const int k0 = s * split;
+          dec.push_back({WORK_DECODE, i, g, 0, 1, k0, std::min(nk, k0 + split), n_parts + g * ns + s});
         }
       n_parts += cfg.n_kv_heads * ns;
     }
   }
-  // heaviest first: chunk tiles by (rows x keys), then decode splits
+  // heaviest chunk tiles first (rows x keys)
   std::stable_sort(work.begin(), work.end(), [](const AttnWork &a, const AttnWork &c) {
     return (long)a.qn * a.k1 > (long)c.qn * c.k1;
   });
+  n_chunk = (int)work.size();
   work.insert(work.end(), dec.begin(), dec.end());
 }
 
@@ -142,7 +153,9 @@ void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const
 
 extern "C" {
 
-const char *orthrus_last_error(const orthrus_engine *eng) { return eng ? eng->err.c_str() : ""; }
+static std::string g_create_err;  // last failed orthrus_create
+
+const char *orthrus_last_error(const orthrus_engine *eng) { return eng ? eng->err.c_str() : g_create_err.c_str(); }
 
 static void free_all(orthrus_engine *e) {
   for (auto &m : e->marks) {
@@ -191,12 +204,14 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
   eng->w.layers = eng->layers.data();
   eng->kc = (uint16_t *)k_pages;
   eng->vc = (uint16_t *)v_pages;
-  auto bail = [&](orthrus_status s) {
+  auto bail = [&](orthrus_status s, const char *what, hipError_t r) {
+    g_create_err = std::string(what) + ": " + hipGetErrorString(r);
     free_all(eng);
     delete eng;
     return s;
   };
-  if (hipGetDevice(&eng->device) != hipSuccess) return bail(ORTHRUS_EHIP);
+  hipError_t r = hipGetDevice(&eng->device);
+  if (r != hipSuccess) return bail(ORTHRUS_EHIP, "hipGetDevice", r);
   const size_t T = c.max_tokens, d = c.d_model;
   const size_t qkvd = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * hd, qd = (size_t)c.n_q_heads * hd;
   struct {
@@ -215,13 +230,16 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
       {(void **)&eng->inv_freq, (size_t)hd / 2 * 8},
   };
   for (auto &a : allocs)
-    if (hipMalloc(a.p, a.bytes) != hipSuccess) return bail(ORTHRUS_ENOMEM);
-  if (hipMemset(eng->U32, 0, T * (size_t)std::max(3 * c.lora_rank, 8) * 4) != hipSuccess) return bail(ORTHRUS_EHIP);
+    if ((r = hipMalloc(a.p, a.bytes)) != hipSuccess) return bail(ORTHRUS_ENOMEM, "hipMalloc", r);
+  if ((r = hipMemset(eng->U32, 0, T * (size_t)std::max(3 * c.lora_rank, 8) * 4)) != hipSuccess)
+    return bail(ORTHRUS_EHIP, "hipMemset", r);
   std::vector<double> inv(hd / 2);
   for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / hd);
-  if (hipMemcpy(eng->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice) != hipSuccess)
-    return bail(ORTHRUS_EHIP);
-  if (hipEventCreateWithFlags(&eng->staged, hipEventDisableTiming) != hipSuccess) return bail(ORTHRUS_EHIP);
+  if ((r = hipMemcpy(eng->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice)) != hipSuccess)
+    return bail(ORTHRUS_EHIP, "hipMemcpy", r);
+  if ((r = hipEventCreateWithFlags(&eng->staged, hipEventDisableTiming)) != hipSuccess)
+    return bail(ORTHRUS_EHIP, "hipEventCreate", r);
+  g_create_err.clear();
   *out = eng;
   return ORTHRUS_OK;
 }
@@ -266,11 +284,16 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   const int T = p.n_tokens;
   if (T == 0) return ORTHRUS_OK;
 
-  int n_parts = 0;
-  build_attn_work(c, *batch, p, eng->work, eng->items, n_parts);
+  int n_parts = 0, n_chunk = 0;
+  build_attn_work(c, *batch, p, eng->work, eng->items, n_chunk, n_parts);
+  const int n_dec_work = (int)eng->work.size() - n_chunk;
   std::vector<int32_t> dec_items;
+  bool multi_split = false;  // some decode row needs the combine kernel
   for (int i = 0; i < batch->n_items; ++i)
-    if (batch->items[i].kind == ORTHRUS_DECODE) dec_items.push_back(i);
+    if (batch->items[i].kind == ORTHRUS_DECODE) {
+      dec_items.push_back(i);
+      multi_split |= eng->items[i].n_parts > 1;
+    }
 
   HIPCHK(hipSetDevice(eng->device), "hipSetDevice");
   hipStream_t s = (hipStream_t)stream;
@@ -373,12 +396,18 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
          "gemm_qkv");
     LCHK(launch_rope_kv(eng->qkv, d_pos, d_slot, eng->inv_freq, kc, vc, T, Hq, Hkv, hd, c.page_size, s),
          "rope_kv");
-    LCHK(launch_attention(eng->qkv, qkvd, kc, vc, d_pages, d_items, d_work, (int)eng->work.size(),
-                          eng->part_ml, eng->part_o, eng->o, qd, Hq, Hkv, hd, c.page_size, s),
-         "attention");
-    LCHK(launch_attn_combine(d_items, d_dec, (int)dec_items.size(), eng->part_ml, eng->part_o, eng->o, qd,
-                             Hq, Hkv, hd, s),
-         "attn_combine");
+    if (n_chunk > 0)
+      LCHK(launch_attn_chunk(eng->qkv, qkvd, kc, vc, d_pages, d_items, d_work, n_chunk, eng->o, qd, Hq, Hkv,
+                             hd, c.page_size, s),
+           "attn_chunk");
+    if (n_dec_work > 0)
+      LCHK(launch_attn_decode(eng->qkv, qkvd, kc, vc, d_pages, d_items, d_work + n_chunk, n_dec_work,
+                              eng->part_ml, eng->part_o, eng->o, qd, Hq, Hkv, hd, c.page_size, s),
+           "attn_decode");
+    if (multi_split)
+      LCHK(launch_attn_combine(d_items, d_dec, (int)dec_items.size(), eng->part_ml, eng->part_o, eng->o, qd,
+                               Hq, Hkv, hd, s),
+           "attn_combine");
     if (lora) {
       LCHK(launch_lora_shrink(eng->o, qd, (const uint16_t *)L.lora_a_o, TE, r, qd, c.lora_scale, eng->U32, eng->U,
                               s),

@@ -1,5 +1,6 @@
-// Ragged causal attention over the paged KV cache, one launch for every
-// item type, plus the log-sum-exp combine of decode splits.
+// Ragged causal attention over the paged KV cache: a chunk kernel for
+// embedding and prefill chunks, a decode kernel for single-row items, and
+// the log-sum-exp combine of decode splits.
 //
 // Efficient Iterative Retrieval with Heterogeneous Batching: §3.2 Batch
 // Unit (embedding chunks, prefill chunks and decode rows share one pass and
@@ -10,18 +11,21 @@
 // left in the cache).  Row j of an item with context c sits at position
 // c + j and sees keys 0 .. c + j; query head h reads KV head h / (Hq/Hkv).
 //
-// Work entries (built on the host, heaviest first):
+// Work entries (built on the host):
 //  CHUNK  : 128 (token, head) rows of one item and KV head.  Scores are
 //           formed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMAs with K
 //           staged in LDS; P^T stays in registers and O^T = V^T P^T reads a
 //           transposed V tile from LDS.  Online softmax in fp32 (exp2).
-//  DECODE : one decode row, one KV head, up to 128 keys; each wave issues
-//           all K and V loads of its 32 keys at once (HD/8 lanes per key,
-//           16-byte loads over the contiguous page_size x HD blocks) and
-//           serves all grouped query heads from one read; the four waves
-//           merge in LDS and write one (max, sum, unnormalised output)
-//           partial, or the finished output when one split covers the whole
-//           context.
+//  DECODE : one decode row, one KV head, one split of its keys.  Head dims
+//           64 and 128: each wave streams 16-key blocks with the next
+//           block's loads in flight; S^T = K Q^T on 16x16x32 bf16 MFMAs
+//           (the grouped query heads are the 16 columns), P passes through
+//           LDS to the V layout and P.V runs as packed bf16 dot products
+//           over key pairs.  Head dims 16 and 32: each wave loads its 32
+//           keys at once (HD/8 lanes per key) and scores with packed dot
+//           products.  The four waves merge in LDS and write one (max, sum,
+//           unnormalised output) partial, or the finished output when one
+//           split covers the whole context.
 #include "device_common.h"
 #include "orthrus_internal.h"
 
@@ -219,7 +223,7 @@ template <int HD, int G>
 struct DecodeSmem {
   float o[ATTN_WAVES][G * HD];
   float ml[ATTN_WAVES][G][2];
-  int pages[ATTN_SPLIT + 2];
+  int pages[DEC_SPLIT_VEC + 2];
 };
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
@@ -228,6 +232,38 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 __device__ __forceinline__ float dot2(uint32_t q2, uint32_t k2, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q2), __builtin_bit_cast(bf16x2_t, k2), c,
                                          false);
+}
+
+// Merge the four waves' (max, sum, unnormalised output) records of one
+// decode split and write either the finished output row (the split covers
+// the whole context) or the split's partial for the combine kernel.
+template <int HD, int G>
+__device__ void finish_decode(const AttnArgs &a, const AttnWork &w, const DevItem &it,
+                              const float (*o)[G * HD], const float (*ml)[G][2]) {
+  const bool whole = (w.k0 == 0 && w.k1 == it.ctx + 1);
+  for (int t = threadIdx.x; t < G * HD; t += 256) {
+    const int h = t / HD, d = t % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < ATTN_WAVES; ++v) M = fmaxf(M, ml[v][h][0]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int v = 0; v < ATTN_WAVES; ++v) {
+      if (ml[v][h][0] == -INFINITY) continue;  // a wave with no keys
+      const float wgt = exp2f(ml[v][h][0] - M);
+      L += wgt * ml[v][h][1];
+      O += wgt * o[v][t];
+    }
+    if (whole) {
+      a.o[(size_t)it.row0 * a.ld_o + (w.kvh * G + h) * HD + d] = (uint16_t)f2bf(O / L);
+    } else {
+      a.part_o[((size_t)w.part * G + h) * HD + d] = O;
+      if (d == 0) {
+        a.part_ml[((size_t)w.part * G + h) * 2 + 0] = M;
+        a.part_ml[((size_t)w.part * G + h) * 2 + 1] = L;
+      }
+    }
+  }
 }
 
 // Decode work: keys [k0, k1) (at most 128) of one decode row and one KV
@@ -241,7 +277,7 @@ template <int HD, int G>
 __device__ void decode_path(const AttnArgs &a, const AttnWork &w, DecodeSmem<HD, G> &sm) {
   constexpr int LPK = HD / 8;                  // lanes per key
   constexpr int KPI = 64 / LPK;                // keys per wave load
-  constexpr int WK = ATTN_SPLIT / ATTN_WAVES;  // keys per wave
+  constexpr int WK = DEC_SPLIT_VEC / ATTN_WAVES;  // keys per wave
   constexpr int NL = WK / KPI > 0 ? WK / KPI : 1;
   static_assert(NL * KPI >= WK, "wave key span");
   const DevItem it = a.items[w.item];
@@ -336,41 +372,210 @@ __device__ void decode_path(const AttnArgs &a, const AttnWork &w, DecodeSmem<HD,
     }
   }
   __syncthreads();
-  const bool whole = (w.k0 == 0 && w.k1 == it.ctx + 1);
-  for (int t = threadIdx.x; t < G * HD; t += 256) {
-    const int h = t / HD, d = t % HD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < ATTN_WAVES; ++v) M = fmaxf(M, sm.ml[v][h][0]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int v = 0; v < ATTN_WAVES; ++v) {
-      if (sm.ml[v][h][0] == -INFINITY) continue;  // a wave with no keys
-      const float wgt = exp2f(sm.ml[v][h][0] - M);
-      L += wgt * sm.ml[v][h][1];
-      O += wgt * sm.o[v][t];
-    }
-    if (whole) {
-      a.o[(size_t)it.row0 * a.ld_o + (w.kvh * G + h) * HD + d] = (uint16_t)f2bf(O / L);
-    } else {
-      a.part_o[((size_t)w.part * G + h) * HD + d] = O;
-      if (d == 0) {
-        a.part_ml[((size_t)w.part * G + h) * 2 + 0] = M;
-        a.part_ml[((size_t)w.part * G + h) * 2 + 1] = L;
-      }
-    }
-  }
+  finish_decode<HD, G>(a, w, it, sm.o, sm.ml);
+}
+
+// Decode work, head dims 64 and 128: keys [k0, k1) (at most DEC_SPLIT_MAX)
+// of one decode row and one KV head.  The split's page ids are staged in
+// LDS once.  Wave w walks the 16-key blocks w, w + 4, ... with the K and V
+// loads of its next block in flight while the current block is consumed.
+//  - K operand: lane l holds key l % 16 of the block, head-dim chunk
+//    (l / 16) + 4 j for k-slice j; Q^T is the B operand with the G grouped
+//    heads as columns (slots G..15 zero).  The 16x16 fp32 result gives lane
+//    l the scores of keys 4 (l / 16) .. +3 for head l % 16.
+//  - Online softmax per head in the score layout: the block maximum over
+//    the four lane groups, the rescale factor alpha and p = 2^(s - m).
+//  - p and alpha go through a per-wave LDS slot to the V layout (lane l:
+//    head-dim chunk l % (HD/8), keys NL (l / (HD/8)) .. +NL-1), where the
+//    accumulators are rescaled only when some alpha differs from 1 and
+//    P.V runs as v_dot2 over (p_i, p_i+1) x (v_i, v_i+1) pairs, p rounded
+//    to bf16 like the P operand of the chunk path.
+template <int HD, int G>
+struct DecodeMfmaSmem {
+  float o[ATTN_WAVES][G * HD];
+  float ml[ATTN_WAVES][G][2];
+  float pb[ATTN_WAVES][G][16];
+  float al[ATTN_WAVES][16];
+  int pages[DEC_SPLIT_MAX + 2];
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int HD, int G>
-__global__ __launch_bounds__(256, 3) void attention_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) union {
-    ChunkSmem<HD> c;
-    DecodeSmem<HD, G> d;
-  } sm;
-  const AttnWork w = a.work[blockIdx.x];
-  if (w.type == WORK_CHUNK) chunk_path<HD>(a, w, sm.c);
-  else decode_path<HD, G>(a, w, sm.d);
+__device__ void decode_mfma_path(const AttnArgs &a, const AttnWork &w, DecodeMfmaSmem<HD, G> &sm) {
+  static_assert(HD == 64 || HD == 128, "head dim");
+  constexpr int LPK = HD / 8;   // lanes per key row in the V layout
+  constexpr int KPI = 64 / LPK; // key groups of the V layout
+  constexpr int NL = 16 / KPI;  // keys per lane per block (V)
+  constexpr int NJ = HD / 32;   // MFMA k-slices
+  static_assert(NL % 2 == 0, "key pairs");
+  const DevItem it = a.items[w.item];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pi0 = w.k0 / a.ps;
+  const int npg = (w.k1 - 1) / a.ps - pi0 + 1;
+  for (int t = threadIdx.x; t < npg; t += 256) sm.pages[t] = a.page_ids[it.page_off + pi0 + t];
+  const int qh = lane & 15, qg = lane >> 4;
+  u32x4_t q[NJ];
+  {
+    const uint16_t *qrow =
+        a.qkv + (size_t)it.row0 * a.ld_qkv + (size_t)(w.kvh * G + (qh < G ? qh : 0)) * HD + qg * 8;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (qh < G) v = *(const u32x4_t *)(qrow + j * 32);
+      q[j] = v;
+    }
+  }
+  __syncthreads();
+  const int sub = lane % LPK, kg = lane / LPK;
+  const int nblk = (w.k1 - w.k0 + 15) / 16;
+  float m_run = -INFINITY, l_part = 0.f;
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  auto row_off = [&](int key) -> size_t {
+    const int page = sm.pages[key / a.ps - pi0];
+    return (((size_t)page * a.Hkv + w.kvh) * a.ps + key % a.ps) * HD;
+  };
+  // keys past the split re-read its last key; their scores are masked
+  auto issue = [&](int b, u32x4_t *kr, u32x4_t *vr) {
+    const int base = w.k0 + b * 16;
+    const size_t ko = row_off(min(base + qh, w.k1 - 1)) + qg * 8;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) kr[j] = *(const u32x4_t *)(a.kc + ko + j * 32);
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      vr[i] = *(const u32x4_t *)(a.vc + row_off(min(base + kg * NL + i, w.k1 - 1)) + sub * 8);
+  };
+  auto consume = [&](int b, const u32x4_t *kr, const u32x4_t *vr) {
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[j]),
+                                                     __builtin_bit_cast(bf16x8_t, q[j]), sacc, 0, 0, 0);
+    const int key0 = w.k0 + b * 16 + 4 * qg;
+    float sc[4], mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sc[e] = key0 + e < w.k1 ? sacc[e] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sc[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);  // finite: every block has a valid key
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float p[4], psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = exp2f(sc[e] - m_new);
+      psum += p[e];
+    }
+    l_part = l_part * alpha + psum;
+    if (qh < G) {
+      *(float4 *)&sm.pb[wave][qh][4 * qg] = make_float4(p[0], p[1], p[2], p[3]);
+      if (qg == 0) sm.al[wave][qh] = alpha;
+    }
+    wave_lds_sync();
+    float alh[G];
+    bool rescale = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      alh[h] = sm.al[wave][h];
+      rescale |= alh[h] != 1.f;
+    }
+    if (rescale) {  // uniform: every lane read the same factors
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alh[h];
+    }
+    // (v_i[d], v_i+1[d]) pairs: low halves, then high halves of each word
+    uint32_t x[NL / 2][8];
+#pragma unroll
+    for (int pr = 0; pr < NL / 2; ++pr)
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        x[pr][2 * wd] = __builtin_amdgcn_perm(vr[2 * pr + 1][wd], vr[2 * pr][wd], 0x05040100u);
+        x[pr][2 * wd + 1] = __builtin_amdgcn_perm(vr[2 * pr + 1][wd], vr[2 * pr][wd], 0x07060302u);
+      }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float pv[NL];
+#pragma unroll
+      for (int i = 0; i < NL; ++i) pv[i] = sm.pb[wave][h][kg * NL + i];
+#pragma unroll
+      for (int pr = 0; pr < NL / 2; ++pr) {
+        const bf16x2_t pk = {(__bf16)pv[2 * pr], (__bf16)pv[2 * pr + 1]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[h][e] = __builtin_amdgcn_fdot2_f32_bf16(pk, __builtin_bit_cast(bf16x2_t, x[pr][e]), acc[h][e], false);
+      }
+    }
+    wave_lds_sync();  // the slot is rewritten by the next block
+  };
+  u32x4_t kb[2][NJ], vb[2][NL];
+  int b = wave;
+  if (b < nblk) issue(b, kb[0], vb[0]);
+  while (b < nblk) {
+    if (b + ATTN_WAVES < nblk) issue(b + ATTN_WAVES, kb[1], vb[1]);
+    consume(b, kb[0], vb[0]);
+    b += ATTN_WAVES;
+    if (b >= nblk) break;
+    if (b + ATTN_WAVES < nblk) issue(b + ATTN_WAVES, kb[0], vb[0]);
+    consume(b, kb[1], vb[1]);
+    b += ATTN_WAVES;
+  }
+  // totals over the lane groups, then stage this wave's record
+  float lt = l_part + __shfl_xor(l_part, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+#pragma unroll
+      for (int o = LPK; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+      acc[h][e] = v;
+    }
+    if (kg == 0) {
+      float *dst = &sm.o[wave][h * HD + sub * 8];
+      *(float4 *)dst = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *(float4 *)(dst + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+  if (qh < G && qg == 0) {
+    sm.ml[wave][qh][0] = m_run;  // -inf for a wave with no block
+    sm.ml[wave][qh][1] = lt;
+  }
+  __syncthreads();
+  finish_decode<HD, G>(a, w, it, sm.o, sm.ml);
+}
+
+template <int HD>
+__global__ __launch_bounds__(256, 3) void attn_chunk_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) ChunkSmem<HD> sm;
+  chunk_path<HD>(a, a.work[blockIdx.x], sm);
+}
+
+template <int HD, int G>
+__global__ __launch_bounds__(256, 4) void attn_decode_vec_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) DecodeSmem<HD, G> sm;
+  decode_path<HD, G>(a, a.work[blockIdx.x], sm);
+}
+
+// eight grouped heads at head dim 128 need 64 accumulators per lane: two
+// workgroups per CU instead of three keeps them out of scratch
+template <int HD, int G>
+__global__ __launch_bounds__(256, (HD == 128 && G == 8) ? 2 : 3) void attn_decode_mfma_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) DecodeMfmaSmem<HD, G> sm;
+  decode_mfma_path<HD, G>(a, a.work[blockIdx.x], sm);
 }
 
 // Merge the split partials of each decode row: out = sum_p 2^(m_p - M) o_p /
@@ -446,36 +651,72 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const DevItem *items,
   }
 }
 
-template <int HD>
-static int launch_hd(const AttnArgs &a, int n_work, int G, hipStream_t s) {
-  switch (G) {
-    case 1: hipLaunchKernelGGL((attention_kernel<HD, 1>), dim3(n_work), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attention_kernel<HD, 2>), dim3(n_work), dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attention_kernel<HD, 4>), dim3(n_work), dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attention_kernel<HD, 8>), dim3(n_work), dim3(256), 0, s, a); break;
+static AttnArgs attn_args(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
+                          const int32_t *page_ids, const DevItem *items, const AttnWork *work, float *part_ml,
+                          float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps) {
+  AttnArgs a;
+  a.qkv = qkv; a.kc = kc; a.vc = vc; a.page_ids = page_ids; a.items = items; a.work = work;
+  a.part_ml = part_ml; a.part_o = part_o; a.o = o;
+  a.ld_qkv = ld_qkv; a.ld_o = ld_o; a.Hq = Hq; a.Hkv = Hkv; a.ps = ps;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  return a;
+}
+
+int launch_attn_chunk(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
+                      const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
+                      uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps, void *stream) {
+  if (n_work <= 0) return 0;
+  const AttnArgs a = attn_args(qkv, ld_qkv, kc, vc, page_ids, items, work, nullptr, nullptr, o, ld_o, Hq, Hkv,
+                               hd, ps);
+  hipStream_t s = (hipStream_t)stream;
+  switch (hd) {
+    case 16: hipLaunchKernelGGL(attn_chunk_kernel<16>, dim3(n_work), dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL(attn_chunk_kernel<32>, dim3(n_work), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(attn_chunk_kernel<64>, dim3(n_work), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(attn_chunk_kernel<128>, dim3(n_work), dim3(256), 0, s, a); break;
     default: return (int)hipErrorInvalidValue;
   }
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }
 
-int launch_attention(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
-                     const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
-                     float *part_ml, float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd,
-                     int ps, void *stream) {
+template <int HD, int G>
+static void launch_decode_g(const AttnArgs &a, int n_work, hipStream_t s) {
+  if constexpr (HD >= 64)
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<HD, G>), dim3(n_work), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_decode_vec_kernel<HD, G>), dim3(n_work), dim3(256), 0, s, a);
+}
+
+template <int HD>
+static int launch_decode_hd(const AttnArgs &a, int n_work, int G, hipStream_t s) {
+  switch (G) {
+    case 1: launch_decode_g<HD, 1>(a, n_work, s); break;
+    case 2: launch_decode_g<HD, 2>(a, n_work, s); break;
+    case 4: launch_decode_g<HD, 4>(a, n_work, s); break;
+    case 8: launch_decode_g<HD, 8>(a, n_work, s); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  ORTHRUS_LAUNCH_CHECK();
+  return 0;
+}
+
+int decode_split_limit(int hd) { return hd >= 64 ? DEC_SPLIT_MAX : DEC_SPLIT_VEC; }
+
+int launch_attn_decode(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
+                       const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
+                       float *part_ml, float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps,
+                       void *stream) {
   if (n_work <= 0) return 0;
-  AttnArgs a;
-  a.qkv = qkv; a.kc = kc; a.vc = vc; a.page_ids = page_ids; a.items = items; a.work = work;
-  a.part_ml = part_ml; a.part_o = part_o; a.o = o;
-  a.ld_qkv = ld_qkv; a.ld_o = ld_o; a.Hq = Hq; a.Hkv = Hkv; a.ps = ps;
-  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  const AttnArgs a = attn_args(qkv, ld_qkv, kc, vc, page_ids, items, work, part_ml, part_o, o, ld_o, Hq, Hkv,
+                               hd, ps);
   const int G = Hq / Hkv;
   hipStream_t s = (hipStream_t)stream;
   switch (hd) {
-    case 16: return launch_hd<16>(a, n_work, G, s);
-    case 32: return launch_hd<32>(a, n_work, G, s);
-    case 64: return launch_hd<64>(a, n_work, G, s);
-    case 128: return launch_hd<128>(a, n_work, G, s);
+    case 16: return launch_decode_hd<16>(a, n_work, G, s);
+    case 32: return launch_decode_hd<32>(a, n_work, G, s);
+    case 64: return launch_decode_hd<64>(a, n_work, G, s);
+    case 128: return launch_decode_hd<128>(a, n_work, G, s);
   }
   return (int)hipErrorInvalidValue;
 }

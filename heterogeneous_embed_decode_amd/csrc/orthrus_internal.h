@@ -34,11 +34,20 @@ struct DevItem {
 };
 
 constexpr int ATTN_ROWS = 128;       // (token, head) rows per chunk workgroup
-constexpr int ATTN_SPLIT = 128;      // keys per decode workgroup (32 per wave)
 constexpr int ATTN_WAVES = 4;
+constexpr int DEC_SPLIT_VEC = 128;   // keys per decode workgroup, head dims 16 and 32 (32 per wave)
+constexpr int DEC_SPLIT_MIN = 128;   // keys per decode workgroup, head dims 64 and 128: 128 ..
+constexpr int DEC_SPLIT_MAX = 512;   // .. 512, the largest that still gives enough workgroups
+constexpr int DEC_MIN_WGS = 2048;    // decode workgroups wanted before a larger split is taken
 
+// keys per decode workgroup the decode kernel accepts for a head dim
+int decode_split_limit(int hd);
+
+// Work list: chunk entries (heaviest first), then decode entries;
+// n_chunk counts the former.
 void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const HostPack &p,
-                     std::vector<AttnWork> &work, std::vector<DevItem> &items, int &n_parts);
+                     std::vector<AttnWork> &work, std::vector<DevItem> &items, int &n_chunk,
+                     int &n_parts);
 
 // ---- kernel launchers (kernels_*.hip) -------------------------------------
 struct LoraArgs {
@@ -63,10 +72,13 @@ int launch_rmsnorm(const float *x, const uint16_t *g, uint16_t *h, int T, int d,
 int launch_rope_kv(uint16_t *qkv, const int32_t *pos, const int32_t *slot,
                    const double *inv_freq, uint16_t *kc, uint16_t *vc, int T, int Hq, int Hkv,
                    int hd, int ps, void *stream);
-int launch_attention(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
-                     const int32_t *page_ids, const DevItem *items, const AttnWork *work,
-                     int n_work, float *part_ml, float *part_o, uint16_t *o, int ld_o,
-                     int Hq, int Hkv, int hd, int ps, void *stream);
+int launch_attn_chunk(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
+                      const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
+                      uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps, void *stream);
+int launch_attn_decode(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
+                       const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
+                       float *part_ml, float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd,
+                       int ps, void *stream);
 int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_dec,
                         const float *part_ml, const float *part_o, uint16_t *o, int ld_o,
                         int Hq, int Hkv, int hd, void *stream);

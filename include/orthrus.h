@@ -175,7 +175,9 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch,
                             int32_t *n_logits, int32_t *n_emb, float *hidden_out,
                             void *stream);
 
-/* Message of the last failed call on this engine ("" if none). */
+/* Message of the last failed call on this engine ("" if none).  With
+ * eng == NULL: the message of the last orthrus_create that failed in this
+ * process ("" if none); not synchronised between threads. */
 const char *orthrus_last_error(const orthrus_engine *eng);
 
 /* Free the engine's workspace.  Waits for its pending work. */
