@@ -28,8 +28,8 @@ struct GemmArgs {
   const uint16_t *U;
   const uint16_t *Bx;
   int ldu, r, lrows, sec1, sec2;
-  // stream-K (residual epilogue only): 0 = one workgroup per output tile;
-  // otherwise the number of workgroups sharing the tile x K-step space
+  // residual epilogue only: 0 = one workgroup per output tile; otherwise
+  // the grid size, whole tiles first and the rest as stream-K slices
   int sk_grid;
   int group_m;  // tile rows per group of the tile order (0 = default)
 };
@@ -255,7 +255,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   const int nk = (g.K + BK - 1) / BK;
   const bool lora_tile_possible = !DUAL && g.U != nullptr;
   // epilogue: lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane/32) + e%4
-  auto epilogue = [&](const bool atomic) {
+  // residual: hardware float atomic add into x (no return value to wait
+  // for); stream-K partial sums of one tile land in no fixed order
+  auto epilogue = [&]() {
     const int jc = lane & 31;
     const int rbase = (lane >> 5) * 4;
 #pragma unroll
@@ -287,8 +289,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
             const float v = acc[i][j][e];
             if (EPI == EPI_BF16) ((uint16_t *)g.C)[o] = (uint16_t)f2bf(g.alpha * v);
             else if (EPI == EPI_F32) ((float *)g.C)[o] = g.alpha * v;
-            else if (atomic) unsafeAtomicAdd((float *)g.C + o, v);
-            else ((float *)g.C)[o] += v;
+            else unsafeAtomicAdd((float *)g.C + o, v);  // residual: x += v
           }
         }
       }
@@ -303,20 +304,34 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
       __builtin_amdgcn_s_barrier();  // all waves are done with the last stage
       run_phase(1, g.ldu, 0, (g.ldu + BK - 1) / BK);
     }
-    epilogue(false);
+    epilogue();
   } else if (EPI == EPI_RESID) {
-    // stream-K: equal shares of the P x nk iteration space; partial tiles
-    // are added into the fp32 residual with hardware float atomics (the
-    // summation order of the partials is therefore not fixed)
-    const long total = (long)P * nk;
+    // residual projections on a grid of sk_grid workgroups (one per CU):
+    // whole tiles first, q consecutive tiles of the grouped order per
+    // workgroup, then the tiles left over shared out as equal slices of
+    // their K-steps (stream-K)
     const int w = xcd_remap(blockIdx.x, g.sk_grid);
+    const int q = P / g.sk_grid;
+    const int P_dp = q * g.sk_grid;
+    for (int t = w * q; t < (w + 1) * q; ++t) {
+      set_tile(t);
+      zero_acc();
+      __builtin_amdgcn_s_barrier();  // the previous tile's stages are retired
+      run_phase(0, g.K, 0, nk);
+      if (lora_tile_possible && m0 < g.lrows) {
+        __builtin_amdgcn_s_barrier();
+        run_phase(1, g.ldu, 0, (g.ldu + BK - 1) / BK);
+      }
+      epilogue();
+    }
+    const long total = (long)(P - P_dp) * nk;
     long it = total * w / g.sk_grid;
     const long it_end = total * (w + 1) / g.sk_grid;
     while (it < it_end) {
       const int t = (int)(it / nk);
       const int kb = (int)(it % nk);
       const int ke = (int)min((long)nk, kb + (it_end - it));
-      set_tile(t);
+      set_tile(P_dp + t);
       zero_acc();
       __builtin_amdgcn_s_barrier();  // previous segment's stages are retired
       run_phase(0, g.K, kb, ke);
@@ -324,7 +339,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
         __builtin_amdgcn_s_barrier();
         run_phase(1, g.ldu, 0, (g.ldu + BK - 1) / BK);
       }
-      epilogue(true);
+      epilogue();
       it += ke - kb;
     }
   }
@@ -388,8 +403,8 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
       if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_F32>(a, s);
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_F32>(a, s);
     case EPI_RESID:
-      // residual projections have few output tiles (N = d): stream-K over
-      // one workgroup per CU keeps every CU busy to the end
+      // residual projections have few output tiles (N = d): one workgroup
+      // per CU, whole tiles in L2-friendly order, the remainder stream-K
       if (big) return launch_cfg<256, 256, 4, 2, 64, 2, EPI_RESID>(a, s, cu_count());
       if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_RESID>(a, s);
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);

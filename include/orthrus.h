@@ -209,7 +209,9 @@ orthrus_status orthrus_fill_hash_bf16(void *dst, uint64_t n, uint32_t seed, uint
 
 /* Standalone bf16 GEMM on the MFMA kernels of the step (device pointers):
  *   C = A B^T with A [M][K] (lda), B [N][K] (ldb), fp32 accumulation.
- * epilogue: 0 store C as bf16 [M][N] (ldc); 1 store fp32; 2 fp32 C += A B^T;
+ * epilogue: 0 store C as bf16 [M][N] (ldc); 1 store fp32; 2 fp32 C += A B^T
+ *             by float atomic adds (large problems split K over workgroups,
+ *             so the partial sums land in no fixed order);
  *           3 SwiGLU: B holds 2N rows at ldb (gate rows 0..N-1, up rows
  *             N..2N-1 at row offset b_up_row), C bf16 = silu(gate) * up.
  * K must be a multiple of 8.  Returns EINVAL for bad sizes, EHIP on
