@@ -68,17 +68,17 @@ def kernel_work(cfg, batch, meta):
     }
 
 
-def kernel_source_digest():
+def kernel_source_digest(name):
     h = hashlib.sha256()
-    p = os.path.join(ROOT, "heterogeneous_embed_decode_amd", "csrc", "kernels_gemm.hip")
-    h.update(open(p, "rb").read())
+    h.update(open(os.path.join(ROOT, "heterogeneous_embed_decode_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}_one_layer_traffic.md")
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel on this workload, if it was taken on the current kernel
+    source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(p):
         return None
     rec = {}
@@ -86,7 +86,8 @@ def traffic_from_profiles(kernel):
         if ":" in line and not line.startswith(("|", "#", " ", "`")):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("kernel_source_sha256_16") != kernel_source_digest():
+    src = rec.get("kernel_source_file")
+    if not src or rec.get("kernel_source_sha256_16") != kernel_source_digest(src):
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
@@ -288,8 +289,7 @@ def main():
         achieved, peak, unit, bound = fl / avg_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
     else:
         achieved, peak, unit, bound = by / avg_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
-    # the committed counter summary covers the one-layer workload only
-    traffic = traffic_from_profiles(dom) if args.workload == "one_layer" else None
+    traffic = traffic_from_profiles(dom, args.workload)
     roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic,
             "algorithmic_per_launch": fl if bound == "mfma" else by, "avg_ms": round(avg_s * 1e3, 5)}
@@ -298,6 +298,7 @@ def main():
         a_avg = prof["attn_decode"]["total_ms"] / prof["attn_decode"]["count"] * 1e-3
         roof["attn_decode_hbm_gbs"] = round(work["attn_decode"][1] / a_avg / 1e9, 1)
         roof["attn_decode_hbm_frac"] = round(work["attn_decode"][1] / a_avg / 1e9 / PEAK_HBM_GBS, 4)
+        roof["attn_decode_traffic"] = traffic_from_profiles("attn_decode", args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:
