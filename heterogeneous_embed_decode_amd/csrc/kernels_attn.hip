@@ -42,24 +42,64 @@ struct AttnArgs {
   float *part_o;
   uint16_t *o;
   int ld_qkv, ld_o, Hq, Hkv, ps;
+  int ps_log2;  // log2(ps) when ps is a power of two, else -1
   float scale_log2;
 };
 
-constexpr int KT = 32;  // keys per chunk-path tile
+// page index and in-page offset of a key (shifts for power-of-two pages;
+// the branch is uniform over the launch)
+__device__ __forceinline__ int page_of(const AttnArgs &a, int key) {
+  return a.ps_log2 >= 0 ? key >> a.ps_log2 : key / a.ps;
+}
+__device__ __forceinline__ int slot_of(const AttnArgs &a, int key) {
+  return a.ps_log2 >= 0 ? key & (a.ps - 1) : key % a.ps;
+}
 
+constexpr int CKT = 64;  // keys per chunk-path tile
+
+// Chunk-path LDS: two buffers of one 64-key tile of K and of V, both in
+// the cache's [key][head dim] order with 16-byte chunks swizzled per key.
+// V rows are padded with zeros to 32 dims for head dims below 32.
 template <int HD>
 struct ChunkSmem {
-  static constexpr int VTS = KT + 4;                // padded row of the transposed V tile
-  static constexpr int VROWS = HD < 32 ? 32 : HD;   // MFMA blocks are 32 rows of the head dim
-  uint16_t K[KT * HD];
-  uint16_t Vt[VROWS * VTS];
+  static constexpr int VD = HD < 32 ? 32 : HD;
+  uint16_t K[2][CKT * HD];
+  uint16_t V[2][CKT * VD];
 };
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// LDS stores of this thread have landed, then the workgroup barrier; no
+// wait on global loads in flight (which __syncthreads' fence would add),
+// and a compiler barrier for LDS accesses
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 16-byte chunk swizzle of a V row: ds_read_b64_tr_b16 lets 16 lanes read
+// 4 consecutive keys x 32 bytes; XOR with 2 (key & 3) puts those 4 rows on
+// distinct banks.  Rows of fewer than 8 chunks are not swizzled.
+template <int VCH>
+__device__ __forceinline__ int vswz(int key) { return VCH >= 8 ? 2 * (key & 3) : 0; }
+
+// Chunk work: 128 (token, head) rows of one item and KV head (32 query
+// rows per wave), keys in 64-key tiles.  The K and V chunks of tile t+1 are
+// loaded into registers (and the page ids of tile t+2 looked up) while tile
+// t is consumed from LDS; one barrier per tile publishes the next buffer.
+//  S^T = K Q^T    : 32x32x16 MFMAs, K rows from LDS (ds_read_b128), Q^T in
+//                   registers for the whole item.
+//  softmax        : online, fp32, exp2 domain, per query row (lane column).
+//  O^T += V^T P^T : P^T is the S^T accumulator packed to bf16 (its key
+//                   order within a 16-key step is 4h..4h+3, 8+4h..8+4h+3 for
+//                   lane half h); the V^T operand takes exactly those keys
+//                   with two ds_read_b64_tr_b16, whose 16-lane groups turn
+//                   4 keys x 4 dims per lane into 4 keys of one dim per lane.
 template <int HD>
 __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &sm) {
-  constexpr int NCH = HD / 8;          // 16-byte chunks per key row
-  constexpr int VTS = ChunkSmem<HD>::VTS;
-  constexpr int NDB = HD < 32 ? 1 : HD / 32;  // 32-wide blocks of the head dim
+  constexpr int NCH = HD / 8;                       // 16-byte chunks per K row
+  constexpr int VD = ChunkSmem<HD>::VD;
+  constexpr int VCH = VD / 8;                       // chunks per V row
+  constexpr int NDB = VD / 32;                      // 32-dim blocks of O^T
+  constexpr int NLD = (CKT * NCH + 255) / 256;      // chunks per thread per tile (each of K and V)
   const int G = a.Hq / a.Hkv;
   const DevItem it = a.items[w.item];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -70,6 +110,8 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
   const bool rvalid = (r / G) < w.qn;
   const int rpos = it.ctx + tok;
   const int nkeys = it.ctx + w.q0 + w.qn;
+  const int ntiles = (nkeys + CKT - 1) / CKT;
+  const int32_t *pages = a.page_ids + it.page_off;
 
   bf16x8_t q[HD / 16];
   {
@@ -81,81 +123,121 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
       q[kk] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
+  if (HD < 32) {  // V dims HD..31 stay zero in both buffers
+    for (int c = tid; c < 2 * CKT * (VD - HD) / 8; c += 256) {
+      const int b = c / (CKT * (VD - HD) / 8), rem = c % (CKT * (VD - HD) / 8);
+      const int key = rem / ((VD - HD) / 8), ch = NCH + rem % ((VD - HD) / 8);
+      *(u32x4_t *)(&sm.V[b][key * VD + ch * 8]) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // this thread's chunks of a tile: chunk i = tid + 256 j is key i / NCH,
+  // head-dim chunk i % NCH (keys past the item re-read its last key)
+  u32x4_t kreg[NLD], vreg[NLD];
+  int pg[NLD];
+  auto chunk_ok = [&](int j) { return NLD * 256 == CKT * NCH || tid + 256 * j < CKT * NCH; };
+  auto lookup = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j)
+      if (chunk_ok(j)) pg[j] = pages[page_of(a, min(t * CKT + (tid + 256 * j) / NCH, nkeys - 1))];
+  };
+  auto load = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      if (!chunk_ok(j)) continue;
+      const int i = tid + 256 * j;
+      const int p = min(t * CKT + i / NCH, nkeys - 1);
+      const size_t off = (((size_t)pg[j] * a.Hkv + w.kvh) * a.ps + slot_of(a, p)) * HD + (i % NCH) * 8;
+      kreg[j] = *(const u32x4_t *)(a.kc + off);
+      vreg[j] = *(const u32x4_t *)(a.vc + off);
+    }
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      if (!chunk_ok(j)) continue;
+      const int i = tid + 256 * j;
+      const int key = i / NCH, c = i % NCH;
+      *(u32x4_t *)(&sm.K[b][key * HD + ((c ^ (key & (NCH - 1))) * 8)]) = kreg[j];
+      *(u32x4_t *)(&sm.V[b][key * VD + ((c ^ vswz<VCH>(key)) * 8)]) = vreg[j];
+    }
+  };
+
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const int32_t *pages = a.page_ids + it.page_off;
   const int min_rpos = it.ctx + w.q0;
-  if (HD < 32) {  // rows HD..31 of the transposed V tile stay zero
-    for (int c = tid; c < (32 - HD) * VTS; c += 256) sm.Vt[HD * VTS + c] = 0;
-  }
 
-  for (int kt0 = 0; kt0 < nkeys; kt0 += KT) {
-    __syncthreads();
-    // stage K (swizzled) and V (transposed) for keys kt0 .. kt0+KT-1
-    for (int c = tid; c < KT * NCH; c += 256) {
-      const int key = c / NCH, dc = c % NCH;
-      const int p = kt0 + key;
-      u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (p < nkeys) {
-        const int page = pages[p / a.ps];
-        const size_t off = (((size_t)page * a.Hkv + w.kvh) * a.ps + p % a.ps) * HD + dc * 8;
-        kv = *(const u32x4_t *)(a.kc + off);
-        vv = *(const u32x4_t *)(a.vc + off);
-      }
-      *(u32x4_t *)(&sm.K[key * HD + ((dc ^ (key & (NCH - 1))) * 8)]) = kv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm.Vt[(dc * 8 + 2 * e) * VTS + key] = (uint16_t)(vv[e] & 0xffffu);
-        sm.Vt[(dc * 8 + 2 * e + 1) * VTS + key] = (uint16_t)(vv[e] >> 16);
-      }
+  lookup(0);
+  load(0);
+  if (ntiles > 1) lookup(1);
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = t & 1;
+    store(b);
+    if (t + 1 < ntiles) {
+      load(t + 1);
+      if (t + 2 < ntiles) lookup(t + 2);
     }
-    __syncthreads();
+    lds_barrier();
+    const int kt0 = t * CKT;
+    const uint16_t *Kt = sm.K[b];
+    const uint16_t *Vt = sm.V[b];
 
-    // S^T for two 32-key blocks
-    f32x16_t s[KT / 32];
+    // S^T for the tile's two 32-key blocks
+    f32x16_t s[CKT / 32];
 #pragma unroll
-    for (int kb = 0; kb < KT / 32; ++kb) {
+    for (int kb = 0; kb < CKT / 32; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
       const int key = kb * 32 + (lane & 31);
 #pragma unroll
       for (int kk = 0; kk < HD / 16; ++kk) {
         const int ch = kk * 2 + half;
-        const bf16x8_t kop = __builtin_bit_cast(
-            bf16x8_t, *(const u32x4_t *)(&sm.K[key * HD + ((ch ^ (key & (NCH - 1))) * 8)]));
+        const bf16x8_t kop =
+            __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(&Kt[key * HD + ((ch ^ (key & (NCH - 1))) * 8)]));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[kk], s[kb], 0, 0, 0);
       }
     }
-    // mask, scale, tile max
-    const bool need_mask = (kt0 + KT - 1) > min_rpos || !rvalid;
+    // scale, causal mask (only tiles that reach past the first row's
+    // position need it; it also hides the clamped keys past the item),
+    // tile max.  Query rows past the chunk compute on zero q and are
+    // never written.
     float mt = -INFINITY;
+    if (kt0 + CKT - 1 > min_rpos) {
 #pragma unroll
-    for (int kb = 0; kb < KT / 32; ++kb)
+      for (int kb = 0; kb < CKT / 32; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kt0 + kb * 32 + (e / 4) * 8 + half * 4 + (e % 4);
-        float v = s[kb][e] * a.scale_log2;
-        if (need_mask && (!rvalid || key > rpos)) v = -INFINITY;
-        s[kb][e] = v;
-        mt = fmaxf(mt, v);
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt0 + kb * 32 + (e / 4) * 8 + half * 4 + (e % 4);
+          const float v = key > rpos ? -INFINITY : s[kb][e] * a.scale_log2;
+          s[kb][e] = v;
+          mt = fmaxf(mt, v);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < CKT / 32; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[kb][e] *= a.scale_log2;
+          mt = fmaxf(mt, s[kb][e]);
+        }
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
     float lsum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KT / 32; ++kb)
+    for (int kb = 0; kb < CKT / 32; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(s[kb][e] - m_use);
-        s[kb][e] = p;
-        lsum += p;
+        const float pr = __builtin_amdgcn_exp2f(s[kb][e] - m_use);
+        s[kb][e] = pr;
+        lsum += pr;
       }
     l_run = l_run * alpha + lsum;
 #pragma unroll
@@ -164,23 +246,27 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
       for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
 
     // O^T += V^T P^T in 16-key steps
+    const int g = lane >> 4, jj = lane & 15;
 #pragma unroll
-    for (int st = 0; st < KT / 16; ++st) {
+    for (int st = 0; st < CKT / 16; ++st) {
       const int kb = st / 2, e0 = (st % 2) * 8;
-      u32x4_t pw;
+      bf16x8_t pop;  // v_cvt_pk_bf16_f32, round to nearest even
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pw[i] = pack_bf2(s[kb][e0 + 2 * i], s[kb][e0 + 2 * i + 1]);
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw);
-      const int kbase = st * 16 + half * 4;
+      for (int i = 0; i < 8; ++i) pop[i] = (__bf16)s[kb][e0 + i];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int dr = db * 32 + (lane & 31);
-        const u32x2_t lo = *(const u32x2_t *)(&sm.Vt[dr * VTS + kbase]);
-        const u32x2_t hi = *(const u32x2_t *)(&sm.Vt[dr * VTS + kbase + 8]);
+        const int dim = db * 32 + (g & 1) * 16 + 4 * (jj & 3);
+        u32x2_t vv[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int key = st * 16 + rr * 8 + 4 * half + (jj >> 2);
+          const uint16_t *src = &Vt[key * VD + (((dim >> 3) ^ vswz<VCH>(key)) * 8) + (dim & 7)];
+          const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(src));
+          vv[rr] = __builtin_bit_cast(u32x2_t, v);
+        }
         u32x4_t vw;
-        vw[0] = lo[0]; vw[1] = lo[1]; vw[2] = hi[0]; vw[3] = hi[1];
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pop,
-                                                           oacc[db], 0, 0, 0);
+        vw[0] = vv[0][0]; vw[1] = vv[0][1]; vw[2] = vv[1][0]; vw[3] = vv[1][1];
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pop, oacc[db], 0, 0, 0);
       }
     }
   }
@@ -283,8 +369,8 @@ __device__ void decode_path(const AttnArgs &a, const AttnWork &w, DecodeSmem<HD,
   const DevItem it = a.items[w.item];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPK, kg = lane / LPK;
-  const int pi0 = w.k0 / a.ps;
-  const int npg = (w.k1 - 1) / a.ps - pi0 + 1;
+  const int pi0 = page_of(a, w.k0);
+  const int npg = page_of(a, w.k1 - 1) - pi0 + 1;
   for (int t = threadIdx.x; t < npg; t += 256) sm.pages[t] = a.page_ids[it.page_off + pi0 + t];
   __syncthreads();
   const int wk0 = w.k0 + wave * WK;
@@ -304,8 +390,8 @@ __device__ void decode_path(const AttnArgs &a, const AttnWork &w, DecodeSmem<HD,
 #pragma unroll
     for (int li = 0; li < NL; ++li) {
       const int key = min(wk0 + li * KPI + kg, wk1 - 1);
-      const int page = sm.pages[key / a.ps - pi0];
-      const size_t off = (((size_t)page * a.Hkv * a.ps) + head_off + key % a.ps) * HD + sub * 8;
+      const int page = sm.pages[page_of(a, key) - pi0];
+      const size_t off = (((size_t)page * a.Hkv * a.ps) + head_off + slot_of(a, key)) * HD + sub * 8;
       kr[li] = *(const u32x4_t *)(a.kc + off);
       vr[li] = *(const u32x4_t *)(a.vc + off);
     }
@@ -415,8 +501,8 @@ __device__ void decode_mfma_path(const AttnArgs &a, const AttnWork &w, DecodeMfm
   static_assert(NL % 2 == 0, "key pairs");
   const DevItem it = a.items[w.item];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int pi0 = w.k0 / a.ps;
-  const int npg = (w.k1 - 1) / a.ps - pi0 + 1;
+  const int pi0 = page_of(a, w.k0);
+  const int npg = page_of(a, w.k1 - 1) - pi0 + 1;
   for (int t = threadIdx.x; t < npg; t += 256) sm.pages[t] = a.page_ids[it.page_off + pi0 + t];
   const int qh = lane & 15, qg = lane >> 4;
   u32x4_t q[NJ];
@@ -440,8 +526,8 @@ __device__ void decode_mfma_path(const AttnArgs &a, const AttnWork &w, DecodeMfm
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   auto row_off = [&](int key) -> size_t {
-    const int page = sm.pages[key / a.ps - pi0];
-    return (((size_t)page * a.Hkv + w.kvh) * a.ps + key % a.ps) * HD;
+    const int page = sm.pages[page_of(a, key) - pi0];
+    return (((size_t)page * a.Hkv + w.kvh) * a.ps + slot_of(a, key)) * HD;
   };
   // keys past the split re-read its last key; their scores are masked
   auto issue = [&](int b, u32x4_t *kr, u32x4_t *vr) {
@@ -559,7 +645,7 @@ __device__ void decode_mfma_path(const AttnArgs &a, const AttnWork &w, DecodeMfm
 }
 
 template <int HD>
-__global__ __launch_bounds__(256, 3) void attn_chunk_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) ChunkSmem<HD> sm;
   chunk_path<HD>(a, a.work[blockIdx.x], sm);
 }
@@ -658,6 +744,7 @@ static AttnArgs attn_args(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, c
   a.qkv = qkv; a.kc = kc; a.vc = vc; a.page_ids = page_ids; a.items = items; a.work = work;
   a.part_ml = part_ml; a.part_o = part_o; a.o = o;
   a.ld_qkv = ld_qkv; a.ld_o = ld_o; a.Hq = Hq; a.Hkv = Hkv; a.ps = ps;
+  a.ps_log2 = (ps & (ps - 1)) == 0 ? __builtin_ctz((unsigned)ps) : -1;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
   return a;
 }
