@@ -23,7 +23,6 @@ struct orthrus_engine {
   // workspace
   float *x = nullptr;
   uint16_t *h = nullptr, *qkv = nullptr, *o = nullptr, *act = nullptr, *U = nullptr;
-  float *U32 = nullptr;  // adapter shrink accumulator, zero between uses
   float *hf = nullptr;
   uint16_t *hl = nullptr;
   double *inv_freq = nullptr;
@@ -165,7 +164,7 @@ static void free_all(orthrus_engine *e) {
   e->marks.clear();
   for (auto ev : e->ev_free) (void)hipEventDestroy(ev);
   e->ev_free.clear();
-  void *ptrs[] = {e->x, e->h, e->qkv, e->o, e->act, e->U, e->U32, e->hf, e->hl, e->inv_freq,
+  void *ptrs[] = {e->x, e->h, e->qkv, e->o, e->act, e->U, e->hf, e->hl, e->inv_freq,
                   e->part_ml, e->part_o, e->meta_dev};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
@@ -224,15 +223,12 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
       {(void **)&eng->o, T * qd * 2},
       {(void **)&eng->act, T * (size_t)c.ffn_dim * 2},
       {(void **)&eng->U, T * (size_t)std::max(3 * c.lora_rank, 8) * 2},
-      {(void **)&eng->U32, T * (size_t)std::max(3 * c.lora_rank, 8) * 4},
       {(void **)&eng->hf, T * d * 4},
       {(void **)&eng->hl, T * d * 2},
       {(void **)&eng->inv_freq, (size_t)hd / 2 * 8},
   };
   for (auto &a : allocs)
     if ((r = hipMalloc(a.p, a.bytes)) != hipSuccess) return bail(ORTHRUS_ENOMEM, "hipMalloc", r);
-  if ((r = hipMemset(eng->U32, 0, T * (size_t)std::max(3 * c.lora_rank, 8) * 4)) != hipSuccess)
-    return bail(ORTHRUS_EHIP, "hipMemset", r);
   std::vector<double> inv(hd / 2);
   for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / hd);
   if ((r = hipMemcpy(eng->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice)) != hipSuccess)
@@ -385,8 +381,7 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
       LCHK(launch_rmsnorm(eng->x, (const uint16_t *)L.g_attn, eng->h, T, d, c.rms_eps, s), "rmsnorm");
     LoraArgs la{};
     if (lora) {
-      LCHK(launch_lora_shrink(eng->h, d, (const uint16_t *)L.lora_a_qkv, TE, 3 * r, d, c.lora_scale, eng->U32,
-                              eng->U, s),
+      LCHK(launch_lora_shrink(eng->h, d, (const uint16_t *)L.lora_a_qkv, TE, 3 * r, d, c.lora_scale, eng->U, s),
            "lora_shrink_qkv");
       la.U = eng->U; la.ldu = 3 * r; la.Bx = (const uint16_t *)L.lora_b_qkv; la.r = r; la.rows = TE;
       la.sec1 = qd; la.sec2 = qd + kvd;
@@ -409,8 +404,7 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
                                Hq, Hkv, hd, s),
            "attn_combine");
     if (lora) {
-      LCHK(launch_lora_shrink(eng->o, qd, (const uint16_t *)L.lora_a_o, TE, r, qd, c.lora_scale, eng->U32, eng->U,
-                              s),
+      LCHK(launch_lora_shrink(eng->o, qd, (const uint16_t *)L.lora_a_o, TE, r, qd, c.lora_scale, eng->U, s),
            "lora_shrink_o");
       la.ldu = r; la.Bx = (const uint16_t *)L.lora_b_o; la.sec1 = d; la.sec2 = d;
     }

@@ -397,6 +397,9 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
   switch (epi) {
     case EPI_BF16:
       if (big) return launch_cfg<256, 256, 2, 4, 64, 2, EPI_BF16>(a, s);
+      // few output columns (the adapter shrink, N = 3 x rank): small tiles
+      // so that more workgroups share the long K loop
+      if (N <= 256 && !skinny) return launch_cfg<64, 64, 2, 2, 64, 4, EPI_BF16>(a, s);
       if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_BF16>(a, s);
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_BF16>(a, s);
     case EPI_F32:

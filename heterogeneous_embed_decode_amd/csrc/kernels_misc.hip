@@ -283,91 +283,15 @@ int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, fl
 
 namespace orthrus {
 
-// Adapter shrink, U32[m, j] += sum_{k in split} X[m, k] A[j, k] for m < rows,
-// j < nr (the LoRA "A" projection of the embedding rows; Efficient
-// Iterative Retrieval with Heterogeneous Batching, §2.2 Parameter sharing).
-// Grid (row blocks of 32, K splits), 4 waves: each wave covers a quarter of
-// the block's K range with 32x32x16 bf16 MFMAs on operands read straight
-// from global memory; the waves reduce in LDS and the block adds its
-// partial into U32 with float atomics.  nr <= 64 * LS_NB.
-constexpr int LS_NB = 6;  // up to 192 adapter columns (3 x rank 64)
-
-__global__ __launch_bounds__(256) void lora_shrink_kernel(const uint16_t *X, int ldx, const uint16_t *A, int rows,
-                                                          int nr, int K, int ksplit, float *U32) {
-  extern __shared__ float red_dyn[];  // [4 waves][nb][16][64]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
-  const int m0 = blockIdx.x * 32;
-  const int kper = ((K + ksplit - 1) / ksplit + 63) / 64 * 64;
-  const int kb = blockIdx.y * kper, ke = min(K, kb + kper);
-  const int nb = (nr + 31) / 32;
-  f32x16_t acc[LS_NB];
-#pragma unroll
-  for (int j = 0; j < LS_NB; ++j)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
-  const int row = m0 + (lane & 31);
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-  for (int k = kb + wave * 16; k < ke; k += 64) {
-    const int kk = k + half * 8;
-    const bool kin = kk < ke;
-    const u32x4_t a = (row < rows && kin) ? *(const u32x4_t *)(X + (size_t)row * ldx + kk) : zero4;
-#pragma unroll
-    for (int j = 0; j < LS_NB; ++j) {
-      if (j >= nb) break;
-      const int col = j * 32 + (lane & 31);
-      const u32x4_t b = (col < nr && kin) ? *(const u32x4_t *)(A + (size_t)col * K + kk) : zero4;
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                      __builtin_bit_cast(bf16x8_t, b), acc[j], 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < LS_NB; ++j) {
-    if (j >= nb) break;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) red_dyn[((wave * nb + j) * 16 + e) * 64 + lane] = acc[j][e];
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < nb * 16 * 64; t += 256) {
-    const int j = t / 1024, e = (t / 64) % 16, l = t % 64;
-    const int q = (j * 16 + e) * 64 + l, st = nb * 16 * 64;
-    const float v = red_dyn[q] + red_dyn[st + q] + red_dyn[2 * st + q] + red_dyn[3 * st + q];
-    const int m = m0 + (e / 4) * 8 + (l >> 5) * 4 + (e % 4);
-    const int col = j * 32 + (l & 31);
-    if (m < rows && col < nr) unsafeAtomicAdd(U32 + (size_t)m * nr + col, v);
-  }
-}
-
-// U[m, j] = bf16(scale * U32[m, j]); U32 is cleared for its next use.
-__global__ void lora_convert_kernel(float *U32, uint16_t *U, int n, float scale) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  U[i] = (uint16_t)f2bf(scale * U32[i]);
-  U32[i] = 0.f;
-}
-
+// Adapter shrink U = bf16(s * X A^T) for the embedding rows (the LoRA "A"
+// projection; Efficient Iterative Retrieval with Heterogeneous Batching,
+// §2.2 Parameter sharing): a GEMM with few output columns (3 x rank), run
+// on the projection GEMM kernel with the scale folded into its bf16
+// epilogue.
 int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, int nr, int K, float scale,
-                       float *U32, uint16_t *U, void *stream) {
+                       uint16_t *U, void *stream) {
   if (rows <= 0 || nr <= 0) return 0;
-  if (nr > 32 * LS_NB) return (int)hipErrorInvalidValue;
-  hipStream_t s = (hipStream_t)stream;
-  const int rb = (rows + 31) / 32;
-  int ksplit = 1;
-  while (rb * ksplit < 512 && K / (ksplit * 2) >= 256) ksplit *= 2;
-  const int nb = (nr + 31) / 32;
-  const size_t lds = (size_t)4 * nb * 16 * 64 * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)lora_shrink_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(4 * LS_NB * 16 * 64 * sizeof(float)));
-    if (e != hipSuccess) return (int)e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(lora_shrink_kernel, dim3(rb, ksplit), dim3(256), lds, s, X, ldx, A, rows, nr, K, ksplit, U32);
-  ORTHRUS_LAUNCH_CHECK();
-  const int n = rows * nr;
-  hipLaunchKernelGGL(lora_convert_kernel, dim3((n + 255) / 256), dim3(256), 0, s, U32, U, n, scale);
-  ORTHRUS_LAUNCH_CHECK();
-  return 0;
+  return launch_gemm(X, ldx, A, K, U, nr, rows, nr, K, EPI_BF16, 0, scale, nullptr, stream);
 }
 
 }  // namespace orthrus

@@ -85,7 +85,7 @@ int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_de
 int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_rows, int n_embed,
                       int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream);
 int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, int nr, int K, float scale,
-                       float *U32, uint16_t *U, void *stream);
+                       uint16_t *U, void *stream);
 int launch_hash_fill(uint16_t *dst, uint64_t n, uint32_t seed, uint32_t tensor_id, uint64_t start, void *stream);
 int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, float *wsum,
                 float *kept, float *emb, int d, void *stream);
