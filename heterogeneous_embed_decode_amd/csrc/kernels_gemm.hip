@@ -257,23 +257,38 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   // epilogue: lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane/32) + e%4
   // residual: hardware float atomic add into x (no return value to wait
   // for); stream-K partial sums of one tile land in no fixed order
+  // bf16 outputs: two rows (e, e+1) of the lane's column are converted by
+  // one v_cvt_pk_bf16_f32 and stored as the low and high halves
+  auto store_bf16_pair = [&](int m, int n, float v0, float v1) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_v;
+    const bf16x2_v pk = {(__bf16)v0, (__bf16)v1};
+    const uint32_t w = __builtin_bit_cast(uint32_t, pk);
+    uint16_t *c = (uint16_t *)g.C + (size_t)m * g.ldc + n;
+    if (m < g.M) c[0] = (uint16_t)(w & 0xffffu);
+    if (m + 1 < g.M) c[g.ldc] = (uint16_t)(w >> 16);
+  };
   auto epilogue = [&]() {
     const int jc = lane & 31;
     const int rbase = (lane >> 5) * 4;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       if (DUAL) {
+        // silu(g) u = g u / (1 + 2^(-g log2 e)): v_exp_f32 and v_rcp_f32
 #pragma unroll
         for (int j = 0; j < NI / 2; ++j) {
           const int n = n0 + wn * WCN + j * 32 + jc;
           if (n >= g.N) continue;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
+          for (int e = 0; e < 16; e += 2) {
             const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
-            if (m >= g.M) continue;
-            const float gt = acc[i][j][e], up = acc[i][j + NI / 2][e];
-            const float sg = gt / (1.f + expf(-gt));
-            ((uint16_t *)g.C)[(size_t)m * g.ldc + n] = (uint16_t)f2bf(sg * up);
+            float o2[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const float gt = acc[i][j][e + u], up = acc[i][j + NI / 2][e + u];
+              const float den = 1.f + __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
+              o2[u] = gt * up * __builtin_amdgcn_rcpf(den);
+            }
+            store_bf16_pair(m, n, o2[0], o2[1]);
           }
         }
       } else {
@@ -281,15 +296,22 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
         for (int j = 0; j < NI; ++j) {
           const int n = n0 + wn * WCN + j * 32 + jc;
           if (n >= g.N) continue;
+          if (EPI == EPI_BF16) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
-            if (m >= g.M) continue;
-            const size_t o = (size_t)m * g.ldc + n;
-            const float v = acc[i][j][e];
-            if (EPI == EPI_BF16) ((uint16_t *)g.C)[o] = (uint16_t)f2bf(g.alpha * v);
-            else if (EPI == EPI_F32) ((float *)g.C)[o] = g.alpha * v;
-            else unsafeAtomicAdd((float *)g.C + o, v);  // residual: x += v
+            for (int e = 0; e < 16; e += 2) {
+              const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
+              store_bf16_pair(m, n, g.alpha * acc[i][j][e], g.alpha * acc[i][j][e + 1]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
+              if (m >= g.M) continue;
+              const size_t o = (size_t)m * g.ldc + n;
+              const float v = acc[i][j][e];
+              if (EPI == EPI_F32) ((float *)g.C)[o] = g.alpha * v;
+              else unsafeAtomicAdd((float *)g.C + o, v);  // residual: x += v
+            }
           }
         }
       }
