@@ -180,43 +180,65 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float *x, const u
 }
 
 // Segmented pooling.  Segment s = (row0, n, slot, kind, first, last, ctx,
-// out).  Grid (segment, column block); each thread owns one column and walks
-// the segment's rows in order.  The weight total wsum is read here and
-// updated by pool_wsum_kernel afterwards so no block reads a value another
-// block has already advanced.
+// out).  Grid (segment, block of 256 columns); lane l of each wave owns
+// columns 4l .. 4l+3 of the block (16-byte loads, 1 KB per wave per row)
+// and wave w sums rows w, w+4, ...; the four waves' sums meet in LDS.  The
+// weight total wsum is read here and updated by pool_wsum_kernel
+// afterwards so no block reads a value another block has already advanced.
+// d is a multiple of 8, so a column group never straddles the row end
+// except as a whole.
 __global__ __launch_bounds__(256) void pool_kernel(const float *hf, const int32_t *segs, float *sum,
                                                    const float *wsum, float *kept, float *emb,
                                                    int d) {
+  __shared__ float4 part[4][64];
   const int32_t *sg = segs + blockIdx.x * 8;
   const int row0 = sg[0], n = sg[1], slot = sg[2], kind = sg[3];
   const int first = sg[4], last = sg[5], ctx = sg[6], out = sg[7];
-  const int j = blockIdx.y * blockDim.x + threadIdx.x;
-  if (j >= d) return;
-  const float *col = hf + (size_t)row0 * d + j;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = blockIdx.y * 256 + lane * 4;  // first of this lane's 4 columns
+  const bool cols = j < d;
   if (kind == ORTHRUS_POOL_MEAN || kind == ORTHRUS_POOL_WMEAN) {
-    float s = 0.f;
-    if (kind == ORTHRUS_POOL_MEAN) {
-      for (int r = 0; r < n; ++r) s += col[(size_t)r * d];
-    } else {
-      for (int r = 0; r < n; ++r) s += (float)(ctx + r + 1) * col[(size_t)r * d];
+    float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (cols) {
+      const float *col = hf + (size_t)row0 * d + j;
+#pragma unroll 4
+      for (int r = wave; r < n; r += 4) {
+        const float4 v = *(const float4 *)(col + (size_t)r * d);
+        const float wgt = kind == ORTHRUS_POOL_MEAN ? 1.f : (float)(ctx + r + 1);
+        s4.x += wgt * v.x;
+        s4.y += wgt * v.y;
+        s4.z += wgt * v.z;
+        s4.w += wgt * v.w;
+      }
     }
-    const float prev = first ? 0.f : sum[(size_t)slot * d + j];
-    const float tot = prev + s;
-    sum[(size_t)slot * d + j] = tot;
-    if (last) {
-      const long long n64 = n, c64 = ctx;
-      const long long add = kind == ORTHRUS_POOL_MEAN ? n64 : n64 * c64 + n64 * (n64 + 1) / 2;
-      const float wt = (first ? 0.f : wsum[slot]) + (float)add;
-      emb[(size_t)out * d + j] = tot / wt;
+    part[wave][lane] = s4;
+    __syncthreads();
+    if (wave != 0 || !cols) return;
+    const float4 a = part[0][lane], b = part[1][lane], c = part[2][lane], e = part[3][lane];
+    float tot[4] = {a.x + b.x + c.x + e.x, a.y + b.y + c.y + e.y, a.z + b.z + c.z + e.z, a.w + b.w + c.w + e.w};
+    float *sp = sum + (size_t)slot * d + j;
+    const long long n64 = n, c64 = ctx;
+    const long long add = kind == ORTHRUS_POOL_MEAN ? n64 : n64 * c64 + n64 * (n64 + 1) / 2;
+    const float wt = (first ? 0.f : wsum[slot]) + (float)add;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tot[q] += first ? 0.f : sp[q];
+      sp[q] = tot[q];
+      if (last) emb[(size_t)out * d + j + q] = tot[q] / wt;
     }
   } else {
+    if (wave != 0 || !cols) return;
     float *k = kept + (size_t)slot * d + j;
-    if (kind == ORTHRUS_POOL_CLS) {
-      if (first) *k = col[0];
-    } else {
-      *k = col[(size_t)(n - 1) * d];
+    const float *src = hf + (size_t)row0 * d + j;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (kind == ORTHRUS_POOL_CLS) {
+        if (first) k[q] = src[q];
+      } else {
+        k[q] = src[(size_t)(n - 1) * d + q];
+      }
+      if (last) emb[(size_t)out * d + j + q] = k[q];
     }
-    if (last) emb[(size_t)out * d + j] = *k;
   }
 }
 
