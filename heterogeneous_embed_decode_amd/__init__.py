@@ -85,7 +85,7 @@ def _load():
                                    _vp, _vp, ctypes.POINTER(_vp)]
     lib.orthrus_create.restype = ctypes.c_int
     lib.orthrus_step.argtypes = [_vp, ctypes.POINTER(orthrus_batch), ctypes.POINTER(orthrus_pool_state),
-                                 _vp, _i32, _vp, _i32, _i32p, _i32p, _vp, _vp]
+                                 _vp, _i32, _vp, _i32, _i32p, _i32p, _i32p, _i32p, _vp, _vp]
     lib.orthrus_step.restype = ctypes.c_int
     lib.orthrus_last_error.argtypes = [_vp]
     lib.orthrus_last_error.restype = ctypes.c_char_p
@@ -177,12 +177,22 @@ def orthrus_create(cfg: orthrus_model_cfg, tok_emb, lm_head, g_final, layers, k_
 
 
 def orthrus_step(eng, batch: BatchArgs, pool_sum, pool_wsum, pool_kept, logits, logits_cap_rows,
-                 emb, emb_cap_rows, hidden_out=None, stream=None):
-    """Returns (status, n_logits, n_emb)."""
+                 emb, emb_cap_rows, hidden_out=None, stream=None, logit_req_ids=None, emb_req_ids=None):
+    """Returns (status, n_logits, n_emb).  logit_req_ids / emb_req_ids:
+    optional int32 numpy arrays of at least logits_cap_rows / emb_cap_rows
+    entries that receive the req_id of each output row."""
     ps = orthrus_pool_state(pool_sum, pool_wsum, pool_kept)
     nl, ne = _i32(0), _i32(0)
+
+    def ids(a, cap):
+        if a is None:
+            return None
+        assert a.dtype == np.int32 and a.flags.c_contiguous and a.size >= cap
+        return a.ctypes.data_as(_i32p)
+
     st = LIB.orthrus_step(eng, ctypes.byref(batch.struct), ctypes.byref(ps), logits, logits_cap_rows,
-                          emb, emb_cap_rows, ctypes.byref(nl), ctypes.byref(ne), hidden_out, stream)
+                          emb, emb_cap_rows, ctypes.byref(nl), ctypes.byref(ne),
+                          ids(logit_req_ids, logits_cap_rows), ids(emb_req_ids, emb_cap_rows), hidden_out, stream)
     return st, nl.value, ne.value
 
 

@@ -250,7 +250,8 @@ void orthrus_destroy(orthrus_engine *eng) {
 
 orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, const orthrus_pool_state *pool,
                             float *logits, int32_t logits_cap_rows, float *emb, int32_t emb_cap_rows,
-                            int32_t *n_logits, int32_t *n_emb, float *hidden_out, void *stream) {
+                            int32_t *n_logits, int32_t *n_emb, int32_t *logit_req_ids, int32_t *emb_req_ids,
+                            float *hidden_out, void *stream) {
   if (!eng) return ORTHRUS_EINVAL;
   eng->err.clear();
   if (!batch || !pool) {
@@ -277,6 +278,13 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   }
   if (n_logits) *n_logits = G;
   if (n_emb) *n_emb = p.n_emb;
+  if (logit_req_ids)
+    for (int k = 0; k < G; ++k) logit_req_ids[k] = batch->items[p.row_item[p.logit_rows[k]]].req_id;
+  if (emb_req_ids) {
+    int k = 0;
+    for (int i = 0; i < batch->n_items; ++i)
+      if (batch->items[i].kind == ORTHRUS_EMBED && batch->items[i].is_last) emb_req_ids[k++] = batch->items[i].req_id;
+  }
   const int T = p.n_tokens;
   if (T == 0) return ORTHRUS_OK;
 

@@ -68,6 +68,8 @@ class DeviceModel:
         self.logits = torch.empty((max_items, dims.vocab), dtype=torch.float32, device=self.device)
         self.emb = torch.empty((max_items, d), dtype=torch.float32, device=self.device)
         self.hidden = torch.empty((max_tokens, d), dtype=torch.float32, device=self.device)
+        self.logit_req = np.zeros(max_items, np.int32)
+        self.emb_req = np.zeros(max_items, np.int32)
 
     def step_args(self, batch):
         return BatchArgs(batch.items_array(), batch.token_ids, batch.page_ids)
@@ -81,7 +83,8 @@ class DeviceModel:
         st, nl, ne = orthrus_step(self.eng, a, self.pool_sum.data_ptr(), self.pool_wsum.data_ptr(),
                                   self.pool_kept.data_ptr(), self.logits.data_ptr(),
                                   self.logits.shape[0], self.emb.data_ptr(), self.emb.shape[0],
-                                  self.hidden.data_ptr() if want_hidden else None, stream)
+                                  self.hidden.data_ptr() if want_hidden else None, stream,
+                                  self.logit_req, self.emb_req)
         return st, nl, ne
 
     def step_checked(self, batch, want_hidden=False):
@@ -89,7 +92,8 @@ class DeviceModel:
         if st != OK:
             raise OrthrusError(st, orthrus_last_error(self.eng))
         torch.cuda.synchronize(self.device)
-        out = {"logits": self.logits[:nl].cpu().numpy(), "emb": self.emb[:ne].cpu().numpy()}
+        out = {"logits": self.logits[:nl].cpu().numpy(), "emb": self.emb[:ne].cpu().numpy(),
+               "logit_req": self.logit_req[:nl].copy(), "emb_req": self.emb_req[:ne].copy()}
         if want_hidden:
             out["hidden"] = self.hidden[:batch.n_tokens].cpu().numpy()
         return out

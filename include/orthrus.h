@@ -164,6 +164,9 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
  *  emb         device fp32 [emb_cap_rows][d]: embedding items with is_last,
  *              in item order (the pooled vector, not normalised)
  *  n_logits, n_emb   host out: rows written
+ *  logit_req_ids, emb_req_ids   optional host int32 [logits_cap_rows] /
+ *              [emb_cap_rows]: req_id of each logit row / embedding row,
+ *              written before the call returns (NULL to skip)
  *  hidden_out  optional device fp32 [n_tokens][d]: residual stream after
  *              the last layer (NULL to skip)
  * Every row appends its K/V at its slot; pooling state is updated.
@@ -172,8 +175,8 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
 orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch,
                             const orthrus_pool_state *pool, float *logits,
                             int32_t logits_cap_rows, float *emb, int32_t emb_cap_rows,
-                            int32_t *n_logits, int32_t *n_emb, float *hidden_out,
-                            void *stream);
+                            int32_t *n_logits, int32_t *n_emb, int32_t *logit_req_ids,
+                            int32_t *emb_req_ids, float *hidden_out, void *stream);
 
 /* Message of the last failed call on this engine ("" if none).  With
  * eng == NULL: the message of the last orthrus_create that failed in this

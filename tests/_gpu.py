@@ -54,6 +54,8 @@ def run_and_compare(dims, dev, orc, batch, check_kv=True, dtype=np.float32, tag=
     res = {}
     assert got["logits"].shape == ref.logits.shape, (got["logits"].shape, ref.logits.shape)
     assert got["emb"].shape == ref.emb.shape, (got["emb"].shape, ref.emb.shape)
+    assert np.array_equal(got["logit_req"], ref.logit_req), (tag, "logit req ids")
+    assert np.array_equal(got["emb_req"], ref.emb_req), (tag, "embedding req ids")
     res["hidden"] = rel_l2(got["hidden"], ref.hidden)
     if ref.logits.size:
         res["logits"] = rel_l2(got["logits"], ref.logits)
