@@ -425,7 +425,11 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
       if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_BF16>(a, s);
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_BF16>(a, s);
     case EPI_F32:
-      if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_F32>(a, s);
+      // the LM head: with few rows it streams the weights, so 64x64 tiles
+      // (two workgroups per CU, twice the loads in flight); with many rows
+      // it is a plain large GEMM
+      if (skinny) return launch_cfg<64, 64, 2, 2, 64, 4, EPI_F32>(a, s);
+      if (big) return launch_cfg<256, 256, 2, 4, 64, 2, EPI_F32>(a, s);
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_F32>(a, s);
     case EPI_RESID:
       // residual projections have few output tiles (N = d): one workgroup

@@ -42,9 +42,9 @@ def pages_needed(cfg, ctxs, extra_chunks=()):
 
 def expected_split(cfg, ctxs):
     """The split the library picks: the largest of 512/256/128 keys that
-    still gives 2048 decode workgroups."""
+    still gives 4096 decode workgroups."""
     split = 512 if cfg.head_dim >= 64 else 128
-    while split > 128 and cfg.n_kv_heads * sum((int(c) + split) // split for c in ctxs) < 2048:
+    while split > 128 and cfg.n_kv_heads * sum((int(c) + split) // split for c in ctxs) < 4096:
         split //= 2
     return split
 
@@ -54,7 +54,7 @@ CASES = [
     ("hd128-g4-ps16-split512",
      sm.ModelConfig(n_layers=1, d_model=512, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn_dim=512,
                     vocab=512, page_size=16, rope_theta=1e6),
-     [0, 1, 15, 16, 17, 63, 64, 65, 511, 512, 513, 1023] + list(np.random.default_rng(1).integers(1000, 3000, 60)),
+     [0, 1, 15, 16, 17, 63, 64, 65, 511, 512, 513, 1023] + list(np.random.default_rng(1).integers(1000, 3000, 130)),
      [(100, 0)]),
     ("hd128-g8-ps16-split128",
      sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=16, n_kv_heads=2, head_dim=128, ffn_dim=256,
@@ -64,17 +64,17 @@ CASES = [
     ("hd64-g1-ps7-split512",
      sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=8, head_dim=64, ffn_dim=256,
                     vocab=300, page_size=7, rope_theta=1e4),
-     list(np.random.default_rng(3).integers(500, 2500, 120)) + [6, 7, 8, 14, 15],
+     list(np.random.default_rng(3).integers(500, 2500, 170)) + [6, 7, 8, 14, 15],
      [(40, 300)]),
     ("hd64-g2-ps32-split256",
      sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=4, head_dim=64, ffn_dim=256,
                     vocab=300, page_size=32, rope_theta=1e4),
-     list(np.random.default_rng(4).integers(200, 1200, 250)),
+     list(np.random.default_rng(4).integers(200, 1200, 320)),
      [(64, 0), (33, 700)]),
     ("hd128-g1-ps16-split256",
      sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=4, head_dim=128, ffn_dim=256,
                     vocab=300, page_size=16, rope_theta=1e6),
-     list(np.random.default_rng(5).integers(100, 1000, 220)),
+     list(np.random.default_rng(5).integers(100, 1000, 400)),
      []),
     ("hd128-g2-ps5-split128",
      sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=128, ffn_dim=256,
