@@ -99,13 +99,26 @@ def _load():
     lib.orthrus_profile.restype = ctypes.c_int
     lib.orthrus_profile_read.argtypes = [_vp, ctypes.c_char_p, _i32]
     lib.orthrus_profile_read.restype = _i32
+    lib.orthrus_sched_create.argtypes = [_i32, _i32, _i32, _i32p, _i32, _i32, ctypes.POINTER(_vp)]
+    lib.orthrus_sched_create.restype = ctypes.c_int
+    lib.orthrus_sched_submit.argtypes = [_vp, _i32, _i32, _i32p, _i32, _i32, _i32]
+    lib.orthrus_sched_submit.restype = ctypes.c_int
+    lib.orthrus_sched_next.argtypes = [_vp, ctypes.POINTER(orthrus_batch), _i32p]
+    lib.orthrus_sched_next.restype = ctypes.c_int
+    lib.orthrus_sched_commit.argtypes = [_vp, _i32p, _i32]
+    lib.orthrus_sched_commit.restype = ctypes.c_int
+    lib.orthrus_sched_stats.argtypes = [_vp, ctypes.POINTER(ctypes.c_int64)]
+    lib.orthrus_sched_stats.restype = ctypes.c_int
+    lib.orthrus_sched_destroy.argtypes = [_vp]
+    lib.orthrus_sched_destroy.restype = None
     return lib
 
 
 LIB = _load()
 EXPORTS = ("orthrus_pack", "orthrus_create", "orthrus_step", "orthrus_last_error",
            "orthrus_destroy", "orthrus_gemm_bf16", "orthrus_profile", "orthrus_profile_read",
-           "orthrus_fill_hash_bf16")
+           "orthrus_fill_hash_bf16", "orthrus_sched_create", "orthrus_sched_submit",
+           "orthrus_sched_next", "orthrus_sched_commit", "orthrus_sched_stats", "orthrus_sched_destroy")
 
 
 class OrthrusError(RuntimeError):
@@ -224,3 +237,47 @@ def orthrus_profile_read(eng) -> dict:
 
 def orthrus_fill_hash_bf16(dst, n, seed, tensor_id, start=0, stream=None) -> int:
     return LIB.orthrus_fill_hash_bf16(dst, n, seed, tensor_id, start, stream)
+
+
+def orthrus_sched_create(token_budget, chunk, page_size, free_pages, n_pool_slots):
+    """Returns (status, handle)."""
+    fp = np.ascontiguousarray(np.asarray(free_pages, np.int32).reshape(-1))
+    h = _vp()
+    st = LIB.orthrus_sched_create(token_budget, chunk, page_size, fp.ctypes.data_as(_i32p), fp.shape[0],
+                                  n_pool_slots, ctypes.byref(h))
+    return st, h
+
+
+def orthrus_sched_submit(s, req_id, kind, tokens, pool_kind=0, max_new_tokens=0) -> int:
+    t = np.ascontiguousarray(np.asarray(tokens, np.int32).reshape(-1))
+    return LIB.orthrus_sched_submit(s, req_id, kind, t.ctypes.data_as(_i32p), t.shape[0], pool_kind,
+                                    max_new_tokens)
+
+
+def orthrus_sched_next(s):
+    """Returns (status, BatchArgs copy of the batch or None, n_logits)."""
+    b = orthrus_batch()
+    nl = _i32(0)
+    st = LIB.orthrus_sched_next(s, ctypes.byref(b), ctypes.byref(nl))
+    if st != OK or b.n_items == 0:
+        return st, None, 0
+    items = np.ctypeslib.as_array(ctypes.cast(b.items, _i32p), shape=(b.n_items * 10,)).reshape(-1, 10).copy()
+    toks = np.ctypeslib.as_array(b.token_ids, shape=(b.n_tokens,)).copy()
+    pages = np.ctypeslib.as_array(b.page_ids, shape=(b.n_page_ids,)).copy() if b.n_page_ids else \
+        np.zeros(0, np.int32)
+    return st, BatchArgs(items, toks, pages), nl.value
+
+
+def orthrus_sched_commit(s, sampled) -> int:
+    a = np.ascontiguousarray(np.asarray(sampled, np.int32).reshape(-1))
+    return LIB.orthrus_sched_commit(s, a.ctypes.data_as(_i32p) if a.size else None, a.shape[0])
+
+
+def orthrus_sched_stats(s):
+    out = (ctypes.c_int64 * 8)()
+    st = LIB.orthrus_sched_stats(s, out)
+    return st, list(out)
+
+
+def orthrus_sched_destroy(s) -> None:
+    LIB.orthrus_sched_destroy(s)

@@ -224,6 +224,60 @@ orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int3
                                  void *C, int32_t ldc, int32_t M, int32_t N, int32_t K,
                                  int32_t epilogue, int32_t b_up_row, void *stream);
 
+/* ---- Intra-batch scheduler and host step driver (host only) -------------
+ * Full text §4 Intra-Batch Scheduling.  Each call of orthrus_sched_next
+ * builds the next batch: one row for every generation request in its decode
+ * phase (submission order; a decode that needs a KV page when none is free
+ * waits), then the residual token budget filled from the embedding queue and
+ * the generation (prompt) queue.  The queue is chosen by credit
+ * accumulators: a_e += w_e, a_g += w_g with w_e, w_g the queues' unscheduled
+ * input tokens at the start of the fill; the larger credit wins (ties to
+ * embedding) and loses w_e + w_g; a queue empty at the start of a step has
+ * its credit reset.  The chosen queue offers its next request not yet
+ * scheduled in this step, as a chunk of min(C, unscheduled tokens); if that
+ * does not fit the budget, the free pages or (first embedding chunk) the
+ * free pooling slots, the queue closes for the step (strict FCFS) and the
+ * selection's credit change is undone.  The batch lists embedding chunks,
+ * prompt chunks, then decode rows, each in submission order; its page lists
+ * come from the scheduler's FIFO free list (pages return to its back when a
+ * request finishes; pooling slots likewise).  A generation request with
+ * max_new_tokens m takes its first token from the logits of the chunk that
+ * completes its prompt and then runs m - 1 decode rows. */
+typedef struct orthrus_sched orthrus_sched;
+
+/* token_budget B >= 1 rows per step, chunk C >= 1, page_size >= 1;
+ * free_pages: host [n_free_pages], the initial free-list order (copied);
+ * pooling slots 0 .. n_pool_slots-1.  EINVAL on bad arguments. */
+orthrus_status orthrus_sched_create(int32_t token_budget, int32_t chunk, int32_t page_size,
+                                    const int32_t *free_pages, int32_t n_free_pages,
+                                    int32_t n_pool_slots, orthrus_sched **out);
+
+/* Queue a request (tokens copied).  kind ORTHRUS_EMBED (pool_kind one of
+ * ORTHRUS_POOL_*) or ORTHRUS_PREFILL (a generation request, max_new_tokens
+ * >= 1).  EINVAL for a bad kind, pool kind, length or token count, or a
+ * req_id submitted before. */
+orthrus_status orthrus_sched_submit(orthrus_sched *s, int32_t req_id, int32_t kind,
+                                    const int32_t *tokens, int32_t n_tokens, int32_t pool_kind,
+                                    int32_t max_new_tokens);
+
+/* Build the next batch into *out (n_items == 0 when nothing can run).  The
+ * arrays *out points to are owned by the scheduler and stay valid until the
+ * next orthrus_sched_commit.  *n_logits: logit rows of the batch.  ESTATE
+ * while the previous batch has not been committed. */
+orthrus_status orthrus_sched_next(orthrus_sched *s, orthrus_batch *out, int32_t *n_logits);
+
+/* Advance after the batch ran: sampled[k] is the token chosen from logit
+ * row k (the batch's logit rows in item order).  EINVAL unless n_sampled
+ * equals the batch's logit rows; ESTATE without a pending batch. */
+orthrus_status orthrus_sched_commit(orthrus_sched *s, const int32_t *sampled, int32_t n_sampled);
+
+/* out8: embedding requests queued, prompt requests queued, requests
+ * decoding, free pages, free pooling slots, credit a_e, credit a_g,
+ * batch pending (0/1). */
+orthrus_status orthrus_sched_stats(const orthrus_sched *s, int64_t *out8);
+
+void orthrus_sched_destroy(orthrus_sched *s);
+
 #ifdef __cplusplus
 }
 #endif
