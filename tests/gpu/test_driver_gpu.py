@@ -1,0 +1,57 @@
+"""The host step driver end to end: the C++ intra-batch scheduler builds
+each batch, orthrus_step runs it on the GPU, the next decode tokens are the
+argmax of the GPU logits, and the scheduler commits them.  Every step is
+checked against the oracle on the same batch (hidden states, logits, pooled
+embeddings, KV appends, output request ids) until all requests finish."""
+
+import numpy as np
+import pytest
+
+import heterogeneous_embed_decode_amd as hed
+from synth import model as sm
+from synth import workloads as wl
+from tests._gpu import make_pair, run_and_compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _as_batch(b: "hed.BatchArgs") -> wl.Batch:
+    items = [wl.Item(*[int(x) for x in row]) for row in b.items_np]
+    return wl.Batch(items, b.tok_np.copy(), b.pages_np.copy())
+
+
+@pytest.mark.parametrize("budget,chunk", [(48, 16), (96, 7)])
+def test_scheduled_steps_match_oracle(budget, chunk):
+    cfg = sm.TINY.with_(lora_rank=8)
+    bits = sm.make_weights(cfg, seed=5, gain_std=0.1)
+    n_pages, slots = 120, 4
+    rng = np.random.default_rng(budget + chunk)
+    dev, orc = make_pair(cfg, n_pages, bits, max_tokens=budget, max_items=32, slots=slots)
+    st, s = hed.orthrus_sched_create(budget, chunk, cfg.page_size, rng.permutation(n_pages), slots)
+    assert st == hed.OK
+    n_emb = n_gen = 0
+    for k in range(10):
+        if k % 2 == 0:
+            toks = rng.integers(0, cfg.vocab, int(rng.integers(3, 70)))
+            assert hed.orthrus_sched_submit(s, k, wl.EMBED, toks, int(rng.integers(0, 4)), 0) == hed.OK
+            n_emb += 1
+        else:
+            toks = rng.integers(0, cfg.vocab, int(rng.integers(2, 40)))
+            assert hed.orthrus_sched_submit(s, k, wl.PREFILL, toks, 0, int(rng.integers(1, 7))) == hed.OK
+            n_gen += 1
+    embs = 0
+    for step in range(200):
+        st, b, nl = hed.orthrus_sched_next(s)
+        assert st == hed.OK
+        if b is None:
+            break
+        got, ref, _ = run_and_compare(cfg, dev, orc, _as_batch(b), tag=f"driver B={budget} C={chunk} step={step}")
+        embs += got["emb"].shape[0]
+        assert got["logits"].shape[0] == nl
+        sampled = np.argmax(got["logits"], axis=1).astype(np.int32) if nl else np.zeros(0, np.int32)
+        assert hed.orthrus_sched_commit(s, sampled) == hed.OK
+    st, stats = hed.orthrus_sched_stats(s)
+    assert stats[:3] == [0, 0, 0] and stats[3] == n_pages and stats[4] == slots
+    assert embs == n_emb
+    hed.orthrus_sched_destroy(s)
+    dev.close()
