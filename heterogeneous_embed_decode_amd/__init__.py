@@ -93,6 +93,8 @@ def _load():
     lib.orthrus_destroy.restype = None
     lib.orthrus_gemm_bf16.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.orthrus_gemm_bf16.restype = ctypes.c_int
+    lib.orthrus_sample.argtypes = [_vp, ctypes.c_int64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.orthrus_sample.restype = ctypes.c_int
     lib.orthrus_fill_hash_bf16.argtypes = [_vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64, _vp]
     lib.orthrus_fill_hash_bf16.restype = ctypes.c_int
     lib.orthrus_profile.argtypes = [_vp, _i32]
@@ -118,7 +120,8 @@ LIB = _load()
 EXPORTS = ("orthrus_pack", "orthrus_create", "orthrus_step", "orthrus_last_error",
            "orthrus_destroy", "orthrus_gemm_bf16", "orthrus_profile", "orthrus_profile_read",
            "orthrus_fill_hash_bf16", "orthrus_sched_create", "orthrus_sched_submit",
-           "orthrus_sched_next", "orthrus_sched_commit", "orthrus_sched_stats", "orthrus_sched_destroy")
+           "orthrus_sched_next", "orthrus_sched_commit", "orthrus_sched_stats", "orthrus_sched_destroy",
+           "orthrus_sample")
 
 
 class OrthrusError(RuntimeError):
@@ -233,6 +236,12 @@ def orthrus_profile_read(eng) -> dict:
     buf = ctypes.create_string_buffer(n + 1)
     LIB.orthrus_profile_read(eng, buf, n + 1)
     return json.loads(buf.value.decode())
+
+
+def orthrus_sample(logits, ld, n_rows, vocab, tokens, temperature=None, top_p=None, uniforms=None,
+                   stream=None) -> int:
+    """Device pointers; temperature/top_p/uniforms may be None."""
+    return LIB.orthrus_sample(logits, ld, n_rows, vocab, temperature, top_p, uniforms, tokens, stream)
 
 
 def orthrus_fill_hash_bf16(dst, n, seed, tensor_id, start=0, stream=None) -> int:

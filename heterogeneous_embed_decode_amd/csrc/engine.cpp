@@ -510,4 +510,14 @@ orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int3
   return r ? ORTHRUS_EHIP : ORTHRUS_OK;
 }
 
+orthrus_status orthrus_sample(const float *logits, int64_t ld, int32_t n_rows, int32_t vocab,
+                              const float *temperature, const float *top_p, const uint32_t *uniforms,
+                              int32_t *tokens, void *stream) {
+  if (n_rows < 0 || vocab < 1 || ld < vocab) return ORTHRUS_EINVAL;
+  if (n_rows == 0) return ORTHRUS_OK;
+  if (!logits || !tokens || (temperature && !uniforms)) return ORTHRUS_EINVAL;
+  return launch_sample(logits, ld, n_rows, vocab, temperature, top_p, uniforms, tokens, stream) ? ORTHRUS_EHIP
+                                                                                                : ORTHRUS_OK;
+}
+
 }  // extern "C"

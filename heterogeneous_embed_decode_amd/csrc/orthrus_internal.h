@@ -86,6 +86,8 @@ int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_ro
                       int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream);
 int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, int nr, int K, float scale,
                        uint16_t *U, void *stream);
+int launch_sample(const float *logits, int64_t ld, int n_rows, int V, const float *temperature,
+                  const float *top_p, const uint32_t *uniforms, int32_t *tokens, void *stream);
 int launch_hash_fill(uint16_t *dst, uint64_t n, uint32_t seed, uint32_t tensor_id, uint64_t start, void *stream);
 int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, float *wsum,
                 float *kept, float *emb, int d, void *stream);

@@ -224,6 +224,35 @@ orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int3
                                  void *C, int32_t ldc, int32_t M, int32_t N, int32_t K,
                                  int32_t epilogue, int32_t b_up_row, void *stream);
 
+/* Next-token choice for logit rows (full text §3.1: the emit stage hands
+ * every generation request's last-row logits to the sampler; §2.2
+ * Generation: one new token per decoding step).  One workgroup per row.
+ *  logits       device fp32 [n_rows][ld], vocab <= ld valid columns; finite
+ *  temperature  device fp32 [n_rows] or NULL (NULL: greedy for every row).
+ *               A row whose temperature is not > 0 takes the greedy token:
+ *               the index of its largest logit, the lowest among equal ones.
+ *  top_p        device fp32 [n_rows] or NULL (= 1): nucleus share, used as
+ *               P16 = rint(top_p * 65536) clamped to [1, 65536]
+ *  uniforms     device uint32 [n_rows]: one uniform 32-bit draw per row;
+ *               required when temperature is given
+ *  tokens       device int32 [n_rows] out
+ * Rows with temperature T > 0: with s = fp32(log2 e / T) and
+ * t_i = (l_i - max) * s in fp32 (0 at the maximum), token i weighs
+ * q_i = floor(2^(30 + t_i)) (0 below t = -30; 2^f from the fp32 Horner
+ * form of the degree-7 Taylor polynomial of e^(f ln 2), no fused
+ * multiply-add).  The nucleus is the smallest set of highest-weight tokens
+ * (lower index first among equal weights) whose weight reaches
+ * ceil(sum(q) * P16 / 65536); with its mass M and x = floor(M * U / 2^32),
+ * the token is the first in index order whose running nucleus weight
+ * exceeds x.  The result depends on nothing else (no summation order), so
+ * it is reproducible bit for bit.  Asynchronous on `stream`; allocates
+ * nothing.  EINVAL for n_rows < 0, vocab < 1, ld < vocab, NULL logits or
+ * tokens (n_rows > 0), or temperature without uniforms; EHIP on launch
+ * failure. */
+orthrus_status orthrus_sample(const float *logits, int64_t ld, int32_t n_rows, int32_t vocab,
+                              const float *temperature, const float *top_p, const uint32_t *uniforms,
+                              int32_t *tokens, void *stream);
+
 /* ---- Intra-batch scheduler and host step driver (host only) -------------
  * Full text §4 Intra-Batch Scheduling.  Each call of orthrus_sched_next
  * builds the next batch: one row for every generation request in its decode

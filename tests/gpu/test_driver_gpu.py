@@ -1,15 +1,19 @@
 """The host step driver end to end: the C++ intra-batch scheduler builds
 each batch, orthrus_step runs it on the GPU, the next decode tokens are the
-argmax of the GPU logits, and the scheduler commits them.  Every step is
+tokens the GPU sampler (orthrus_sample: greedy rows and temperature/top-p
+rows) picks from the GPU logits, and the scheduler commits them.  Every step is
 checked against the oracle on the same batch (hidden states, logits, pooled
-embeddings, KV appends, output request ids) until all requests finish."""
+embeddings, KV appends, output request ids) and every sampled token against
+the sampling oracle on the same logits, until all requests finish."""
 
 import numpy as np
 import pytest
+import torch
 
 import heterogeneous_embed_decode_amd as hed
 from synth import model as sm
 from synth import workloads as wl
+from oracle.sample import sample as oracle_sample
 from tests._gpu import make_pair, run_and_compare
 
 pytestmark = pytest.mark.gpu
@@ -48,7 +52,19 @@ def test_scheduled_steps_match_oracle(budget, chunk):
         got, ref, _ = run_and_compare(cfg, dev, orc, _as_batch(b), tag=f"driver B={budget} C={chunk} step={step}")
         embs += got["emb"].shape[0]
         assert got["logits"].shape[0] == nl
-        sampled = np.argmax(got["logits"], axis=1).astype(np.int32) if nl else np.zeros(0, np.int32)
+        sampled = np.zeros(0, np.int32)
+        if nl:
+            temp = np.where(np.arange(nl) % 2 == 0, 0.0, 0.8).astype(np.float32)
+            top = np.full(nl, 0.9, np.float32)
+            uni = rng.integers(0, 2 ** 32, nl, dtype=np.uint64).astype(np.uint32)
+            tok = torch.empty(nl, dtype=torch.int32, device=dev.device)
+            t_d, p_d = torch.from_numpy(temp).to(dev.device), torch.from_numpy(top).to(dev.device)
+            u_d = torch.from_numpy(uni.view(np.int32)).to(dev.device)
+            assert hed.orthrus_sample(dev.logits.data_ptr(), cfg.vocab, nl, cfg.vocab, tok.data_ptr(),
+                                      t_d.data_ptr(), p_d.data_ptr(), u_d.data_ptr(),
+                                      torch.cuda.current_stream().cuda_stream) == hed.OK
+            sampled = tok.cpu().numpy()
+            assert np.array_equal(sampled, oracle_sample(got["logits"], temp, top, uni)), step
         assert hed.orthrus_sched_commit(s, sampled) == hed.OK
     st, stats = hed.orthrus_sched_stats(s)
     assert stats[:3] == [0, 0, 0] and stats[3] == n_pages and stats[4] == slots

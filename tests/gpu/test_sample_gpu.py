@@ -1,0 +1,106 @@
+"""orthrus_sample (the GPU sampler) against the sampling oracle, token for
+token: greedy rows, temperature rows with and without a nucleus, rows full
+of tied logits (the tie rule decides the nucleus), vocabularies that are
+ragged against the 4096-token draw tile, the Mistral-7B vocabulary with
+many rows, a Llama-3-sized vocabulary, a padded leading dimension, the
+degenerate temperatures; and the
+error paths."""
+
+import numpy as np
+import pytest
+import torch
+
+import heterogeneous_embed_decode_amd as hed
+from oracle.sample import sample as oracle_sample
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(L, temp, top_p, uni, ld=None):
+    n, V = L.shape
+    ld = ld or V
+    dev = torch.zeros((max(n, 1), ld), dtype=torch.float32, device="cuda:0")
+    dev[:n, :V] = torch.from_numpy(L)
+    tok = torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda:0")
+    t = torch.from_numpy(np.asarray(temp, np.float32)).cuda() if temp is not None else None
+    p = torch.from_numpy(np.asarray(top_p, np.float32)).cuda() if top_p is not None else None
+    u = torch.from_numpy(np.asarray(uni, np.uint32).view(np.int32)).cuda() if uni is not None else None
+    st = hed.orthrus_sample(dev.data_ptr(), ld, n, V, tok.data_ptr(),
+                            t.data_ptr() if t is not None else None,
+                            p.data_ptr() if p is not None else None,
+                            u.data_ptr() if u is not None else None,
+                            torch.cuda.current_stream().cuda_stream)
+    assert st == hed.OK
+    torch.cuda.synchronize()
+    return tok[:n].cpu().numpy()
+
+
+def _case(rng, n, V, temps, tops, scale=3.0, quant=None):
+    L = (rng.standard_normal((n, V)) * scale).astype(np.float32)
+    if quant:
+        L = (np.round(L * quant) / quant).astype(np.float32)
+    temp = rng.choice(np.asarray(temps, np.float32), n)
+    top = rng.choice(np.asarray(tops, np.float32), n)
+    uni = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+    return L, temp, top, uni
+
+
+@pytest.mark.parametrize("n,V,seed", [(1, 1, 0), (7, 37, 1), (16, 2047, 2), (16, 2049, 3), (9, 5000, 4),
+                                        (12, 4097, 6), (3, 128256, 5)])
+def test_sampler_matches_oracle(n, V, seed):
+    rng = np.random.default_rng(seed)
+    print(f"[sample n={n} V={V} seed={seed}]", flush=True)
+    L, temp, top, uni = _case(rng, n, V, [0.0, 0.25, 0.7, 1.0, 1.6], [0.05, 0.5, 0.9, 0.99, 1.0])
+    got = _run(L, temp, top, uni)
+    ref = oracle_sample(L, temp, top, uni)
+    assert np.array_equal(got, ref), (got, ref)
+
+
+def test_sampler_ties_decide_the_nucleus():
+    # logits on a coarse grid: many equal weights, tau falls inside tie groups
+    rng = np.random.default_rng(9)
+    print("[sample ties]", flush=True)
+    L, temp, top, uni = _case(rng, 24, 3000, [0.5, 1.0, 2.0], [0.1, 0.3, 0.6, 0.95], scale=1.0, quant=2)
+    got = _run(L, temp, top, uni)
+    assert np.array_equal(got, oracle_sample(L, temp, top, uni))
+    # all-equal rows: the nucleus is the lowest indices
+    L = np.zeros((4, 1000), np.float32)
+    got = _run(L, [1.0] * 4, [0.01, 0.01, 0.5, 1.0], [0, 2 ** 32 - 1, 2 ** 32 - 1, 2 ** 31])
+    assert got.tolist() == oracle_sample(L, np.ones(4), np.array([0.01, 0.01, 0.5, 1.0], np.float32),
+                                         np.array([0, 2 ** 32 - 1, 2 ** 32 - 1, 2 ** 31], np.uint32)).tolist()
+    assert got.tolist() == [0, 9, 499, 500]
+
+
+def test_sampler_mistral_vocab_many_rows():
+    rng = np.random.default_rng(12)
+    n, V = 96, 32000
+    print(f"[sample n={n} V={V}]", flush=True)
+    L, temp, top, uni = _case(rng, n, V, [0.0, 0.6, 0.8, 1.0, 1.3], [0.8, 0.9, 0.95, 1.0], scale=2.5)
+    got = _run(L, temp, top, uni, ld=32064)
+    ref = oracle_sample(L, temp, top, uni)
+    assert np.array_equal(got, ref)
+
+
+def test_sampler_greedy_and_degenerate():
+    rng = np.random.default_rng(13)
+    L = rng.standard_normal((5, 777)).astype(np.float32)
+    L[1, 100] = L[1, 700] = L[1].max() + 1                  # tie at the maximum
+    got = _run(L, None, None, None)
+    assert np.array_equal(got, np.argmax(L, axis=1))
+    temp = np.array([1e-30, 1e-45, np.inf, -1.0, 0.0], np.float32)
+    uni = np.array([5, 7, 123456789, 0, 0], np.uint32)
+    got = _run(L, temp, np.ones(5, np.float32), uni)
+    assert np.array_equal(got, oracle_sample(L, temp, np.ones(5, np.float32), uni))
+    assert got[1] == 100                                     # the two maxima split U; small U: the first
+
+
+def test_sampler_errors():
+    x = torch.zeros((2, 8), dtype=torch.float32, device="cuda:0")
+    tok = torch.zeros(2, dtype=torch.int32, device="cuda:0")
+    t = torch.ones(2, dtype=torch.float32, device="cuda:0")
+    assert hed.orthrus_sample(x.data_ptr(), 8, 0, 8, tok.data_ptr()) == hed.OK          # no rows
+    assert hed.orthrus_sample(x.data_ptr(), 4, 2, 8, tok.data_ptr()) == hed.EINVAL      # ld < vocab
+    assert hed.orthrus_sample(x.data_ptr(), 8, 2, 0, tok.data_ptr()) == hed.EINVAL      # vocab
+    assert hed.orthrus_sample(x.data_ptr(), 8, -1, 8, tok.data_ptr()) == hed.EINVAL
+    assert hed.orthrus_sample(None, 8, 2, 8, tok.data_ptr()) == hed.EINVAL
+    assert hed.orthrus_sample(x.data_ptr(), 8, 2, 8, tok.data_ptr(), temperature=t.data_ptr()) == hed.EINVAL
