@@ -157,6 +157,51 @@ def cpu_baseline(cfg, batch, n_pages, bits, kv_bits):
                       f"oracle, {dt:.2f} s"}
 
 
+def measure_sampler(dev, cfg, meta, stream, run, calls=50, greedy_too=True):
+    """Time orthrus_sample on the logit rows of the workload's first step
+    (temperature 0.8, top-p 0.9 on every row: the full radix-select path;
+    greedy rows stop after the max pass).  HIP events on the step's stream."""
+    import numpy as np
+    import torch
+    import heterogeneous_embed_decode_amd as hed
+    nl = int(meta["n_logits"])
+    if not nl:
+        return None
+    g = np.random.default_rng(0)
+    temp_d = torch.full((nl,), 0.8, dtype=torch.float32, device="cuda")
+    top_d = torch.full((nl,), 0.9, dtype=torch.float32, device="cuda")
+    uni_d = torch.from_numpy(g.integers(0, 2 ** 32, nl, dtype=np.uint64).astype(np.uint32).view(np.int32)).cuda()
+    tok_d = torch.empty(nl, dtype=torch.int32, device="cuda")
+    sptr = stream.cuda_stream
+    run(1)
+
+    def smp(k, greedy=False):
+        for _ in range(k):
+            st_ = hed.orthrus_sample(dev.logits.data_ptr(), cfg.vocab, nl, cfg.vocab, tok_d.data_ptr(),
+                                     None if greedy else temp_d.data_ptr(), top_d.data_ptr(), uni_d.data_ptr(), sptr)
+            assert st_ == hed.OK
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for mode in (("sampled", "greedy") if greedy_too else ("sampled",)):
+        smp(3, mode == "greedy")
+        e0.record(stream)
+        smp(calls, mode == "greedy")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[mode] = e0.elapsed_time(e1) / calls * 1e3
+    by = nl * cfg.vocab * 4
+    out = {"kernel": "sample_kernel", "rows": nl, "vocab": cfg.vocab, "temperature": 0.8, "top_p": 0.9,
+           "us_per_call": round(res["sampled"], 2), "logit_bytes": by,
+           "hbm_gbs": round(by / (res["sampled"] * 1e-6) / 1e9, 1),
+           "hbm_frac": round(by / (res["sampled"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    if "greedy" in res:
+        out["greedy_us_per_call"] = round(res["greedy"], 2)
+    print(f"sampler: {nl} rows x {cfg.vocab}: " + ", ".join(f"{k} {v:.1f} us" for k, v in res.items()),
+          file=sys.stderr, flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +212,9 @@ def main():
                     help="one_layer (default line): one Mistral-7B-shaped layer, 4160 rows; mix91/mix55/mix19: "
                          "the 32-layer 9:1 (ten distinct steps), 5:5 (rank 64) and Llama-3.1-8B 1:9 workloads")
     ap.add_argument("--layers", type=int, default=32, help="depth of the mixed workloads")
+    ap.add_argument("--sampler-only", action="store_true",
+                    help="run one step of the workload, then time only the sampler on its logit rows "
+                         "(temperature 0.8, top-p 0.9); prints the sampler object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB (read) into 1 GiB (write), 5 times; "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -248,6 +296,10 @@ def main():
                 raise hed.OrthrusError(s, hed.orthrus_last_error(dev.eng))
             rows_done[0] += batches[j].n_tokens
 
+    if args.sampler_only:
+        print(json.dumps({"sampler": measure_sampler(dev, cfg, meta, stream, run, greedy_too=False)}), flush=True)
+        dev.close()
+        return
     run(args.warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -300,6 +352,7 @@ def main():
         roof["attn_decode_hbm_frac"] = round(work["attn_decode"][1] / a_avg / 1e9 / PEAK_HBM_GBS, 4)
         roof["attn_decode_traffic"] = traffic_from_profiles("attn_decode", args.workload)
 
+    sampler = measure_sampler(dev, cfg, meta, stream, run)
     cpu = None
     if not args.no_cpu_baseline:
         print("timing the CPU oracle on the same step ...", file=sys.stderr, flush=True)
@@ -327,6 +380,7 @@ def main():
                    "ffn_dim": cfg.ffn_dim, "vocab": cfg.vocab, "lora_rank": cfg.lora_rank},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "sampler": sampler,
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
