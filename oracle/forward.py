@@ -42,9 +42,14 @@ def widen_weights(bits: dict, dtype=np.float32) -> dict:
     return {k: bf16_bits_to_f32(v).astype(dtype) for k, v in bits.items()}
 
 
-def new_pool(n_slots: int, d: int, dtype=np.float32) -> dict:
-    return {"sum": np.zeros((n_slots, d), dtype), "wsum": np.zeros(n_slots, dtype),
-            "kept": np.zeros((n_slots, d), dtype)}
+def new_pool(n_slots: int, d: int, dtype=np.float32, buf_rows: int = 0) -> dict:
+    """Pooling state; ``buf_rows`` > 0 adds the BUFFER kind's hidden-state
+    buffer [n_slots, buf_rows, d]."""
+    p = {"sum": np.zeros((n_slots, d), dtype), "wsum": np.zeros(n_slots, dtype),
+         "kept": np.zeros((n_slots, d), dtype)}
+    if buf_rows:
+        p["buf"] = np.zeros((n_slots, buf_rows, d), dtype)
+    return p
 
 
 def new_kv(cfg, n_pages: int, dtype=np.float32, k_bits=None, v_bits=None):

@@ -79,7 +79,7 @@ def pack_py(cfg, batch, limits: Limits) -> Dict[str, np.ndarray]:
         if it.kind == EMBED:
             if it.pool_slot < 0 or it.pool_slot >= limits.max_pool_slots:
                 raise PackError(ESTATE, f"item {i}: pool slot out of range")
-            if it.pool_kind not in (0, 1, 2, 3):
+            if it.pool_kind & ~8 not in (0, 1, 2, 3, 4):      # a base kind, optionally | L2 (8)
                 raise PackError(EINVAL, f"item {i}: bad pool kind")
             if it.is_first and it.ctx_len != 0:
                 raise PackError(ESTATE, f"item {i}: first chunk must start at position 0")

@@ -18,7 +18,8 @@ import numpy as np
 from .model import ModelConfig, TINY, MISTRAL_7B
 
 EMBED, PREFILL, DECODE = 0, 1, 2
-POOL_MEAN, POOL_WMEAN, POOL_CLS, POOL_LAST = 0, 1, 2, 3
+POOL_MEAN, POOL_WMEAN, POOL_CLS, POOL_LAST, POOL_BUFFER = 0, 1, 2, 3, 4
+POOL_L2 = 8   # OR-ed into a pool kind: unit-length output
 
 ITEM_FIELDS = ("kind", "req_id", "n_tokens", "ctx_len", "page_off", "n_pages",
                "pool_slot", "pool_kind", "is_first", "is_last")

@@ -1,11 +1,14 @@
 """Pins of the incremental pooler: closed forms of the weight totals,
-chunk-invariance of the streaming sum, and the kept-state heads."""
+chunk-invariance of the streaming sum, the kept-state heads, the buffered
+head (every row kept at its position, the mean over the whole input at the
+end, the same function as the streaming mean) and the L2 flag (unit
+length, same direction, constant rows give h / |h|, zero stays zero)."""
 
 import numpy as np
 import pytest
 
 import oracle
-from synth.workloads import Item, EMBED, POOL_MEAN, POOL_WMEAN, POOL_CLS, POOL_LAST
+from synth.workloads import Item, EMBED, POOL_MEAN, POOL_WMEAN, POOL_CLS, POOL_LAST, POOL_BUFFER, POOL_L2
 
 RNG = np.random.default_rng(7)
 
@@ -78,3 +81,46 @@ def test_unfinished_chunk_returns_nothing_and_keeps_state():
               pool_kind=POOL_WMEAN, is_first=1, is_last=0)
     assert oracle.pool_item(pool, it, H) is None
     assert pool["wsum"][0] == 36
+
+
+def _run_chunks_buf(kind, H, chunks, dtype=np.float64, rows=None):
+    pool = oracle.new_pool(4, H.shape[1], dtype, buf_rows=rows or H.shape[0])
+    n, off, out = H.shape[0], 0, None
+    for c in chunks:
+        it = Item(kind=EMBED, req_id=1, n_tokens=c, ctx_len=off, pool_slot=2,
+                  pool_kind=kind, is_first=int(off == 0), is_last=int(off + c == n))
+        out = oracle.pool_item(pool, it, H[off:off + c].astype(dtype))
+        off += c
+    return out, pool
+
+
+def test_buffer_head_keeps_every_row_and_runs_the_mean_at_the_end():
+    # summary page: an arbitrary head buffers all hidden states (O(nd)) and runs at the end
+    H = RNG.standard_normal((300, 5))
+    for chunks in ([300], [256, 44], [7] * 42 + [6], [1] * 300):
+        e, pool = _run_chunks_buf(POOL_BUFFER, H, chunks, rows=320)
+        np.testing.assert_array_equal(pool["buf"][2, :300], H)          # rows at their positions
+        assert not pool["buf"][2, 300:].any()
+        np.testing.assert_allclose(e, H.mean(axis=0), rtol=1e-12, atol=1e-14)
+        em, _ = _run_chunks(POOL_MEAN, H, chunks)                        # same function as the streaming mean
+        np.testing.assert_allclose(e, em, rtol=1e-12, atol=1e-14)
+    # nothing is emitted before the last chunk
+    pool = oracle.new_pool(4, 5, np.float64, buf_rows=300)
+    it = Item(kind=EMBED, req_id=1, n_tokens=10, ctx_len=0, pool_slot=2, pool_kind=POOL_BUFFER, is_first=1, is_last=0)
+    assert oracle.pool_item(pool, it, H[:10]) is None
+
+
+@pytest.mark.parametrize("kind", [POOL_MEAN, POOL_WMEAN, POOL_CLS, POOL_LAST, POOL_BUFFER])
+def test_l2_flag_normalises_the_head_output(kind):
+    H = RNG.standard_normal((60, 7)) + 0.5
+    e0, _ = _run_chunks_buf(kind, H, [16, 16, 16, 12])
+    e1, _ = _run_chunks_buf(kind | POOL_L2, H, [16, 16, 16, 12])
+    assert abs(np.linalg.norm(e1) - 1.0) < 1e-12
+    np.testing.assert_allclose(e1 * np.linalg.norm(e0), e0, rtol=1e-12, atol=1e-14)   # same direction
+    # constant rows: every head gives h / |h|
+    h = RNG.standard_normal(7)
+    e, _ = _run_chunks_buf(kind | POOL_L2, np.tile(h, (20, 1)), [8, 12])
+    np.testing.assert_allclose(e, h / np.linalg.norm(h), rtol=1e-12)
+    # a zero vector stays zero
+    z, _ = _run_chunks_buf(kind | POOL_L2, np.zeros((5, 7)), [5])
+    assert not z.any()
