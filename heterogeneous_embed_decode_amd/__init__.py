@@ -54,7 +54,7 @@ class orthrus_batch(ctypes.Structure):
 
 
 class orthrus_pool_state(ctypes.Structure):
-    _fields_ = [("sum", _vp), ("wsum", _vp), ("kept", _vp)]
+    _fields_ = [("sum", _vp), ("wsum", _vp), ("kept", _vp), ("buf", _vp), ("buf_rows", _i32)]
 
 
 class orthrus_packed(ctypes.Structure):
@@ -193,11 +193,13 @@ def orthrus_create(cfg: orthrus_model_cfg, tok_emb, lm_head, g_final, layers, k_
 
 
 def orthrus_step(eng, batch: BatchArgs, pool_sum, pool_wsum, pool_kept, logits, logits_cap_rows,
-                 emb, emb_cap_rows, hidden_out=None, stream=None, logit_req_ids=None, emb_req_ids=None):
+                 emb, emb_cap_rows, hidden_out=None, stream=None, logit_req_ids=None, emb_req_ids=None,
+                 pool_buf=None, buf_rows=0):
     """Returns (status, n_logits, n_emb).  logit_req_ids / emb_req_ids:
     optional int32 numpy arrays of at least logits_cap_rows / emb_cap_rows
-    entries that receive the req_id of each output row."""
-    ps = orthrus_pool_state(pool_sum, pool_wsum, pool_kept)
+    entries that receive the req_id of each output row.  pool_buf /
+    buf_rows: the BUFFER pooling kind's hidden-state buffer."""
+    ps = orthrus_pool_state(pool_sum, pool_wsum, pool_kept, pool_buf, buf_rows)
     nl, ne = _i32(0), _i32(0)
 
     def ids(a, cap):

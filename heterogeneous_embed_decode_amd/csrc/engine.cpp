@@ -276,6 +276,12 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
     eng->err = "null output or pool buffer";
     return ORTHRUS_EINVAL;
   }
+  for (size_t k = 0; k < p.pool_segs.size(); k += 8)
+    if ((p.pool_segs[k + 3] & ~ORTHRUS_POOL_L2) == ORTHRUS_POOL_BUFFER &&
+        (!pool->buf || p.pool_segs[k + 6] + p.pool_segs[k + 1] > pool->buf_rows)) {
+      eng->err = "pooling buffer missing or too short for a BUFFER item";
+      return ORTHRUS_ECAPACITY;
+    }
   if (n_logits) *n_logits = G;
   if (n_emb) *n_emb = p.n_emb;
   if (logit_req_ids)
@@ -437,7 +443,8 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
                      0, 1.f, nullptr, s),
          "lm_head");
   if (n_segs)
-    LCHK(launch_pool(eng->hf, d_segs, (int)n_segs, pool->sum, pool->wsum, pool->kept, emb, d, s), "pool");
+    LCHK(launch_pool(eng->hf, d_segs, (int)n_segs, pool->sum, pool->wsum, pool->kept, pool->buf,
+                     pool->buf_rows, emb, d, s), "pool");
   return ORTHRUS_OK;
 }
 

@@ -188,15 +188,49 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float *x, const u
 // d is a multiple of 8, so a column group never straddles the row end
 // except as a whole.
 __global__ __launch_bounds__(256) void pool_kernel(const float *hf, const int32_t *segs, float *sum,
-                                                   const float *wsum, float *kept, float *emb,
-                                                   int d) {
+                                                   const float *wsum, float *kept, float *buf, int buf_rows,
+                                                   float *emb, int d) {
   __shared__ float4 part[4][64];
   const int32_t *sg = segs + blockIdx.x * 8;
-  const int row0 = sg[0], n = sg[1], slot = sg[2], kind = sg[3];
+  const int row0 = sg[0], n = sg[1], slot = sg[2], kind = sg[3] & ~ORTHRUS_POOL_L2;
   const int first = sg[4], last = sg[5], ctx = sg[6], out = sg[7];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = blockIdx.y * 256 + lane * 4;  // first of this lane's 4 columns
   const bool cols = j < d;
+  if (kind == ORTHRUS_POOL_BUFFER) {
+    // keep this chunk's rows at their positions; on the last chunk run the
+    // head over all N rows: wave w sums rows w, w+4, ... in position order
+    // (rows of this chunk read from hf, which holds the same values), the
+    // waves meet in a fixed order, so the sum order depends on N alone
+    float *bs = buf + (size_t)slot * buf_rows * d + j;
+    const float *hs = hf + (size_t)row0 * d + j;
+    if (cols)
+      for (int r = wave; r < n; r += 4) *(float4 *)(bs + (size_t)(ctx + r) * d) = *(const float4 *)(hs + (size_t)r * d);
+    if (!last) return;
+    const int N = ctx + n;
+    float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (cols) {
+#pragma unroll 4
+      for (int r = wave; r < N; r += 4) {
+        const float4 v = r < ctx ? *(const float4 *)(bs + (size_t)r * d) : *(const float4 *)(hs + (size_t)(r - ctx) * d);
+        s4.x += v.x;
+        s4.y += v.y;
+        s4.z += v.z;
+        s4.w += v.w;
+      }
+    }
+    part[wave][lane] = s4;
+    __syncthreads();
+    if (wave != 0 || !cols) return;
+    const float4 a = part[0][lane], b = part[1][lane], c = part[2][lane], e = part[3][lane];
+    const float fN = (float)N;
+    float *o = emb + (size_t)out * d + j;
+    o[0] = (((a.x + b.x) + c.x) + e.x) / fN;
+    o[1] = (((a.y + b.y) + c.y) + e.y) / fN;
+    o[2] = (((a.z + b.z) + c.z) + e.z) / fN;
+    o[3] = (((a.w + b.w) + c.w) + e.w) / fN;
+    return;
+  }
   if (kind == ORTHRUS_POOL_MEAN || kind == ORTHRUS_POOL_WMEAN) {
     float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (cols) {
@@ -246,7 +280,7 @@ __global__ void pool_wsum_kernel(const int32_t *segs, int n_segs, float *wsum) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= n_segs) return;
   const int32_t *sg = segs + s * 8;
-  const int n = sg[1], slot = sg[2], kind = sg[3], first = sg[4], ctx = sg[6];
+  const int n = sg[1], slot = sg[2], kind = sg[3] & ~ORTHRUS_POOL_L2, first = sg[4], ctx = sg[6];
   if (kind != ORTHRUS_POOL_MEAN && kind != ORTHRUS_POOL_WMEAN) {
     if (first) wsum[slot] = 0.f;
     return;
@@ -254,6 +288,31 @@ __global__ void pool_wsum_kernel(const int32_t *segs, int n_segs, float *wsum) {
   const long long n64 = n, c64 = ctx;
   const long long add = kind == ORTHRUS_POOL_MEAN ? n64 : n64 * c64 + n64 * (n64 + 1) / 2;
   wsum[slot] = (first ? 0.f : wsum[slot]) + (float)add;
+}
+
+// Unit L2 length for the finished embeddings whose pool kind carries the
+// L2 flag: one block per segment, e / max(|e|, 1e-12) with the sum of
+// squares accumulated in fp32.
+__global__ __launch_bounds__(256) void pool_l2_kernel(const int32_t *segs, float *emb, int d) {
+  __shared__ float red[4];
+  const int32_t *sg = segs + blockIdx.x * 8;
+  if (!(sg[3] & ORTHRUS_POOL_L2) || !sg[5]) return;
+  float *e = emb + (size_t)sg[7] * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    const float4 v = *(const float4 *)(e + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  const float tot = block_sum_256(ss, red);
+  const float sc = 1.f / fmaxf(sqrtf(tot), 1e-12f);
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    float4 v = *(const float4 *)(e + c);
+    v.x *= sc;
+    v.y *= sc;
+    v.z *= sc;
+    v.w *= sc;
+    *(float4 *)(e + c) = v;
+  }
 }
 
 int launch_embed_rmsnorm(const int32_t *tok, const uint16_t *E, const uint16_t *g, float *x, uint16_t *h, int T,
@@ -289,14 +348,16 @@ int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_ro
   return 0;
 }
 
-int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, float *wsum, float *kept,
-                float *emb, int d, void *stream) {
+int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, float *wsum, float *kept, float *buf,
+                int buf_rows, float *emb, int d, void *stream) {
   if (n_segs <= 0) return 0;
   hipLaunchKernelGGL(pool_kernel, dim3(n_segs, (d + 255) / 256), dim3(256), 0, (hipStream_t)stream, hf,
-                     segs, sum, wsum, kept, emb, d);
+                     segs, sum, wsum, kept, buf, buf_rows, emb, d);
   ORTHRUS_LAUNCH_CHECK();
   hipLaunchKernelGGL(pool_wsum_kernel, dim3((n_segs + 63) / 64), dim3(64), 0, (hipStream_t)stream, segs,
                      n_segs, wsum);
+  ORTHRUS_LAUNCH_CHECK();
+  hipLaunchKernelGGL(pool_l2_kernel, dim3(n_segs), dim3(256), 0, (hipStream_t)stream, segs, emb, d);
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }

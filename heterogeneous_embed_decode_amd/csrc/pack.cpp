@@ -53,7 +53,7 @@ orthrus_status validate_and_pack(const orthrus_model_cfg &cfg, const orthrus_bat
     if (it.kind == ORTHRUS_EMBED) {
       if (it.pool_slot < 0 || it.pool_slot >= cfg.max_pool_slots)
         return fail(err, elen, ORTHRUS_ESTATE, "item %d: pool slot out of range", i);
-      if (it.pool_kind < 0 || it.pool_kind > 3)
+      if ((it.pool_kind & ~ORTHRUS_POOL_L2) < ORTHRUS_POOL_MEAN || (it.pool_kind & ~ORTHRUS_POOL_L2) > ORTHRUS_POOL_BUFFER)
         return fail(err, elen, ORTHRUS_EINVAL, "item %d: bad pool kind", i);
       if (it.is_first && it.ctx_len != 0)
         return fail(err, elen, ORTHRUS_ESTATE, "item %d: first chunk must start at position 0", i);

@@ -123,7 +123,8 @@ void orthrus_sched_destroy(orthrus_sched *s) { delete s; }
 orthrus_status orthrus_sched_submit(orthrus_sched *s, int32_t req_id, int32_t kind, const int32_t *tokens,
                                     int32_t n_tokens, int32_t pool_kind, int32_t max_new_tokens) {
   if (!s || !tokens || n_tokens < 1 || (kind != ORTHRUS_EMBED && kind != ORTHRUS_PREFILL)) return ORTHRUS_EINVAL;
-  if (kind == ORTHRUS_EMBED && (pool_kind < ORTHRUS_POOL_MEAN || pool_kind > ORTHRUS_POOL_LAST))
+  if (kind == ORTHRUS_EMBED && ((pool_kind & ~ORTHRUS_POOL_L2) < ORTHRUS_POOL_MEAN ||
+                                (pool_kind & ~ORTHRUS_POOL_L2) > ORTHRUS_POOL_BUFFER))
     return ORTHRUS_EINVAL;
   if (kind == ORTHRUS_PREFILL && max_new_tokens < 1) return ORTHRUS_EINVAL;
   if (s->ids_seen.count(req_id)) return ORTHRUS_EINVAL;

@@ -31,7 +31,7 @@ class DeviceModel:
     """
 
     def __init__(self, dims, weights, n_pages, max_tokens, max_items, max_pool_slots,
-                 device="cuda:0", kv_bits=None, kv_tensors=None):
+                 device="cuda:0", kv_bits=None, kv_tensors=None, buf_rows=0):
         self.dims = dims
         self.device = torch.device(device)
         torch.cuda.set_device(self.device)
@@ -49,6 +49,10 @@ class DeviceModel:
         self.pool_sum = torch.zeros((max(max_pool_slots, 1), d), dtype=torch.float32, device=self.device)
         self.pool_wsum = torch.zeros(max(max_pool_slots, 1), dtype=torch.float32, device=self.device)
         self.pool_kept = torch.zeros((max(max_pool_slots, 1), d), dtype=torch.float32, device=self.device)
+        # hidden-state buffer of the BUFFER pooling kind: [slots][buf_rows][d]
+        self.buf_rows = buf_rows
+        self.pool_buf = (torch.zeros((max(max_pool_slots, 1), buf_rows, d), dtype=torch.float32, device=self.device)
+                         if buf_rows else None)
         self.max_tokens, self.max_items = max_tokens, max_items
         self.cfg = make_cfg(dims.n_layers, d, dims.n_q_heads, dims.n_kv_heads, dims.head_dim,
                             dims.ffn_dim, dims.vocab, dims.lora_rank, dims.page_size, n_pages,
@@ -84,7 +88,8 @@ class DeviceModel:
                                   self.pool_kept.data_ptr(), self.logits.data_ptr(),
                                   self.logits.shape[0], self.emb.data_ptr(), self.emb.shape[0],
                                   self.hidden.data_ptr() if want_hidden else None, stream,
-                                  self.logit_req, self.emb_req)
+                                  self.logit_req, self.emb_req,
+                                  self.pool_buf.data_ptr() if self.pool_buf is not None else None, self.buf_rows)
         return st, nl, ne
 
     def step_checked(self, batch, want_hidden=False):

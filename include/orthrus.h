@@ -51,8 +51,16 @@ enum { ORTHRUS_EMBED = 0, ORTHRUS_PREFILL = 1, ORTHRUS_DECODE = 2 };
 /* Pooling heads (§3.3 Incremental Pooler; agihunt summary).  MEAN weights
  * every token 1; WMEAN weights a token by its 1-based position in the
  * request; CLS keeps the hidden state at position 0; LAST keeps the hidden
- * state of the request's final token. */
-enum { ORTHRUS_POOL_MEAN = 0, ORTHRUS_POOL_WMEAN = 1, ORTHRUS_POOL_CLS = 2, ORTHRUS_POOL_LAST = 3 };
+ * state of the request's final token.  BUFFER (the summary's arbitrary
+ * deterministic head at O(nd) memory) stores every final hidden state of
+ * the request at its position in the slot's buffer and, on the last chunk,
+ * emits the mean of all N buffered rows, summed in an order fixed by N
+ * alone; the buffer stays readable for any other head.  ORTHRUS_POOL_L2,
+ * OR'ed into any kind, scales the emitted vector to unit L2 length
+ * (e / max(|e|, 1e-12); the OpRAG page's mean-pool-then-normalise
+ * convention). */
+enum { ORTHRUS_POOL_MEAN = 0, ORTHRUS_POOL_WMEAN = 1, ORTHRUS_POOL_CLS = 2, ORTHRUS_POOL_LAST = 3,
+       ORTHRUS_POOL_BUFFER = 4, ORTHRUS_POOL_L2 = 8 };
 
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
@@ -96,7 +104,7 @@ typedef struct {
  *  page_off, n_pages   the request's page list is page_ids[page_off ..
  *              page_off + n_pages); n_pages * page_size >= ctx_len + n_tokens
  *  pool_slot   EMBED only: row of the pooling state
- *  pool_kind   EMBED only: ORTHRUS_POOL_*
+ *  pool_kind   EMBED only: ORTHRUS_POOL_MEAN .. BUFFER, optionally | ORTHRUS_POOL_L2
  *  is_first    EMBED: first chunk (resets the slot; requires ctx_len == 0)
  *  is_last     EMBED: final chunk (emits the embedding); PREFILL: the chunk
  *              completes the prompt (emits logits of its last row) */
@@ -113,11 +121,15 @@ typedef struct {
 } orthrus_batch;
 
 /* Pooling state, device fp32: sum [max_pool_slots][d], wsum
- * [max_pool_slots], kept [max_pool_slots][d].  Carried across steps by the
- * caller; a slot is private to one request between its first and last
- * chunk. */
+ * [max_pool_slots], kept [max_pool_slots][d], and for the BUFFER kind
+ * buf [max_pool_slots][buf_rows][d] (row p of a slot holds the final
+ * hidden state of the request's token p; NULL / 0 when no BUFFER item is
+ * run).  Carried across steps by the caller; a slot is private to one
+ * request between its first and last chunk. */
 typedef struct {
   float *sum, *wsum, *kept;
+  float *buf;
+  int32_t buf_rows;
 } orthrus_pool_state;
 
 /* Host metadata produced by orthrus_pack (all host int32; caller-allocated
@@ -162,7 +174,8 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
  *  logits      device fp32 [logits_cap_rows][vocab]: rows in item order
  *              (prefill items with is_last, then decode items)
  *  emb         device fp32 [emb_cap_rows][d]: embedding items with is_last,
- *              in item order (the pooled vector, not normalised)
+ *              in item order (the pooled vector; unit length when the
+ *              item's pool kind carries ORTHRUS_POOL_L2)
  *  n_logits, n_emb   host out: rows written
  *  logit_req_ids, emb_req_ids   optional host int32 [logits_cap_rows] /
  *              [emb_cap_rows]: req_id of each logit row / embedding row,
@@ -171,7 +184,8 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
  *              the last layer (NULL to skip)
  * Every row appends its K/V at its slot; pooling state is updated.
  * Errors: any orthrus_pack status; ECAPACITY when logits_cap_rows or
- * emb_cap_rows is too small; EHIP/ENOMEM from the runtime. */
+ * emb_cap_rows is too small or a BUFFER item reaches past pool->buf_rows
+ * (or pool->buf is NULL); EHIP/ENOMEM from the runtime. */
 orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch,
                             const orthrus_pool_state *pool, float *logits,
                             int32_t logits_cap_rows, float *emb, int32_t emb_cap_rows,

@@ -213,8 +213,10 @@ def one_layer_workload(seed_len: int = 2, seed_tok: int = 1,
 
 
 def random_batch(cfg: ModelConfig, seed: int, max_items: int = 12, max_len: int = 40,
-                 max_ctx: int = 70, n_pages: Optional[int] = None, n_slots: int = 16):
-    """A random valid ragged batch (for packer and attention coverage tests)."""
+                 max_ctx: int = 70, n_pages: Optional[int] = None, n_slots: int = 16,
+                 pool_kinds=(POOL_MEAN, POOL_WMEAN, POOL_CLS, POOL_LAST)):
+    """A random valid ragged batch (for packer and attention coverage tests);
+    embedding items draw their pool kind from ``pool_kinds``."""
     rng = np.random.default_rng(seed)
     ps = cfg.page_size
     n_e, n_p, n_d = (int(x) for x in rng.integers(0, max_items // 3 + 1, 3))
@@ -242,7 +244,7 @@ def random_batch(cfg: ModelConfig, seed: int, max_items: int = 12, max_len: int 
         it = Item(kind=k, req_id=int(idx * 3 + 5), n_tokens=n, ctx_len=c,
                   page_off=len(pages), n_pages=len(pg),
                   pool_slot=int(slots[idx]) if k == EMBED else -1,
-                  pool_kind=int(rng.integers(0, 4)) if k == EMBED else 0,
+                  pool_kind=int(pool_kinds[int(rng.integers(0, len(pool_kinds)))]) if k == EMBED else 0,
                   is_first=first, is_last=int(rng.integers(0, 2)) if k != DECODE else 1)
         pages.extend(pg)
         toks.extend(int(t) for t in rng.integers(0, cfg.vocab, n))

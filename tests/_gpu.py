@@ -16,16 +16,16 @@ EMB_COS = 0.999
 
 
 def make_pair(dims, n_pages, weights, kv_bits=None, max_tokens=None, max_items=64, slots=16,
-              oracle_dtype=np.float32):
+              oracle_dtype=np.float32, buf_rows=0):
     from heterogeneous_embed_decode_amd.device_model import DeviceModel
     mt = max_tokens or 4096
-    dev = DeviceModel(dims, weights, n_pages, mt, max_items, slots, kv_bits=kv_bits)
+    dev = DeviceModel(dims, weights, n_pages, mt, max_items, slots, kv_bits=kv_bits, buf_rows=buf_rows)
     W = oracle.widen_weights(weights, oracle_dtype)
     if kv_bits is None:
         kv = oracle.new_kv(dims, n_pages, oracle_dtype)
     else:
         kv = oracle.new_kv(dims, n_pages, oracle_dtype, kv_bits[0], kv_bits[1])
-    pool = oracle.new_pool(slots, dims.d_model, oracle_dtype)
+    pool = oracle.new_pool(slots, dims.d_model, oracle_dtype, buf_rows=buf_rows)
     return dev, (W, kv, pool)
 
 

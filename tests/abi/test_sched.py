@@ -69,6 +69,7 @@ def test_scheduler_errors():
     assert st == hed.OK
     assert hed.orthrus_sched_submit(s, 1, DECODE, [1, 2], 0, 0) == hed.EINVAL       # kind
     assert hed.orthrus_sched_submit(s, 1, EMBED, [1, 2], 7, 0) == hed.EINVAL        # pool kind
+    assert hed.orthrus_sched_submit(s, 1, EMBED, [1, 2], 16, 0) == hed.EINVAL       # unknown flag
     assert hed.orthrus_sched_submit(s, 1, PREFILL, [1, 2], 0, 0) == hed.EINVAL      # no new tokens
     assert hed.orthrus_sched_submit(s, 1, EMBED, [], 0, 0) == hed.EINVAL            # empty
     assert hed.orthrus_sched_submit(s, 1, EMBED, [1, 2], 0, 0) == hed.OK

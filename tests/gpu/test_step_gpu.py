@@ -1,7 +1,8 @@
 """Whole-step parity through orthrus_step against the oracle: the small
 multi-step workload (prefill, then three mixed embedding/decode steps),
-LoRA and every pooling head, random ragged batches, the one-layer
-Mistral-7B-shaped batch, degenerate batches and host-side error paths."""
+LoRA and every pooling head (with and without the L2 flag, and the
+buffered head), random ragged batches, the one-layer Mistral-7B-shaped
+batch, degenerate batches and host-side error paths."""
 
 import numpy as np
 import pytest
@@ -15,13 +16,56 @@ from tests._gpu import make_pair, run_and_compare, seed_pool
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("pool_kind", [wl.POOL_MEAN, wl.POOL_WMEAN, wl.POOL_CLS, wl.POOL_LAST])
+@pytest.mark.parametrize("pool_kind", [wl.POOL_MEAN, wl.POOL_WMEAN, wl.POOL_CLS, wl.POOL_LAST, wl.POOL_BUFFER,
+                                       wl.POOL_MEAN | wl.POOL_L2, wl.POOL_LAST | wl.POOL_L2,
+                                       wl.POOL_BUFFER | wl.POOL_L2])
 def test_tiny_multistep(pool_kind):
     cfg, batches, n_pages = wl.tiny_workload(pool_kind=pool_kind)
     bits = sm.make_weights(cfg, seed=0, gain_std=0.1)
-    dev, orc = make_pair(cfg, n_pages, bits)
+    dev, orc = make_pair(cfg, n_pages, bits, buf_rows=64)
     for s, b in enumerate(batches):
-        run_and_compare(cfg, dev, orc, b, tag=f"tiny pool={pool_kind} step={s}")
+        got, _, _ = run_and_compare(cfg, dev, orc, b, tag=f"tiny pool={pool_kind} step={s}")
+        if pool_kind & wl.POOL_L2 and got["emb"].size:
+            assert np.allclose(np.linalg.norm(got["emb"].astype(np.float64), axis=1), 1.0, atol=1e-5)
+    dev.close()
+
+
+def test_buffered_head_keeps_rows_and_means_them():
+    """BUFFER kind: the slot buffer holds every final hidden state at its
+    position (against the oracle), and the emitted vector is the mean of
+    exactly those buffered rows (checked against the GPU's own buffer in
+    fp64, so the head's arithmetic is checked tightly); a request longer
+    than the buffer is refused before any device work."""
+    cfg = sm.TINY.with_(lora_rank=8)
+    bits = sm.make_weights(cfg, seed=6, gain_std=0.1)
+    _, batches, n_pages = wl.tiny_workload(cfg=cfg, pool_kind=wl.POOL_BUFFER)
+    dev, orc = make_pair(cfg, n_pages, bits, buf_rows=48)
+    pool = orc[2]
+    from tests._util import rel_l2
+    for s, b in enumerate(batches):
+        got, ref, _ = run_and_compare(cfg, dev, orc, b, tag=f"buffer step={s}")
+        buf = dev.pool_buf.cpu().numpy()
+        for it in b.items:
+            if it.kind != wl.EMBED:
+                continue
+            n = it.ctx_len + it.n_tokens
+            assert rel_l2(buf[it.pool_slot, :n], pool["buf"][it.pool_slot, :n]) < 2e-2
+        k = 0
+        for it in b.items:
+            if it.kind == wl.EMBED and it.is_last:
+                n = it.ctx_len + it.n_tokens
+                mean = buf[it.pool_slot, :n].astype(np.float64).mean(axis=0)
+                np.testing.assert_allclose(got["emb"][k], mean, rtol=1e-5, atol=1e-6)
+                k += 1
+    # a BUFFER item reaching past buf_rows: ECAPACITY, nothing launched
+    bb = wl.BatchBuilder(cfg, wl.PageAllocator(n_pages, seed=1))
+    bb.add(wl.Request(7, wl.EMBED, list(range(1, 50)), pool_slot=0, pool_kind=wl.POOL_BUFFER))
+    big = bb.build([(7, wl.EMBED, 49, 1, 1)])
+    before = dev.pool_buf.clone()
+    st, _, _ = dev.step(big)
+    assert st == hed.ECAPACITY
+    torch.cuda.synchronize()
+    assert torch.equal(before, dev.pool_buf)
     dev.close()
 
 
@@ -44,10 +88,12 @@ def test_random_ragged_batches(seed):
                            ffn_dim=512, vocab=500, lora_rank=8, page_size=16, rope_theta=1e6),
             sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=2, head_dim=128,
                            ffn_dim=384, vocab=1000, lora_rank=16, page_size=16, rope_theta=1e6)][seed % 4]
-    b, n_pages = wl.random_batch(base, 100 + seed, max_items=15, max_len=150, max_ctx=700)
+    kinds = (wl.POOL_MEAN, wl.POOL_WMEAN, wl.POOL_CLS, wl.POOL_LAST, wl.POOL_BUFFER,
+             wl.POOL_MEAN | wl.POOL_L2, wl.POOL_BUFFER | wl.POOL_L2, wl.POOL_CLS | wl.POOL_L2)
+    b, n_pages = wl.random_batch(base, 100 + seed, max_items=15, max_len=150, max_ctx=700, pool_kinds=kinds)
     bits = sm.make_weights(base, seed=seed, gain_std=0.1)
     kv = wl.synthetic_kv(base, n_pages, seed=3)
-    dev, orc = make_pair(base, n_pages, bits, kv_bits=kv)
+    dev, orc = make_pair(base, n_pages, bits, kv_bits=kv, buf_rows=856)
     seed_pool(dev, orc, seed)
     run_and_compare(base, dev, orc, b, tag=f"random seed={seed}")
     dev.close()
