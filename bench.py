@@ -65,7 +65,32 @@ def kernel_work(cfg, batch, meta):
         "attn_decode": (dec_flops, dec_bytes),
         "lora_shrink_qkv": (2.0 * TE * 3 * r * d, 2.0 * (TE * d + 3 * r * d)),
         "lora_shrink_o": (2.0 * TE * r * qd, 2.0 * (TE * qd + r * qd)),
+        "pool": (0.0, pool_bytes(cfg, batch)),
     }
+
+
+def pool_bytes(cfg, batch):
+    """HBM bytes of the pooling kernels per step: streaming heads read the
+    chunk's fp32 rows once; the buffered head also writes them to the
+    slot's buffer and, on the last chunk, reads the rows buffered by earlier
+    chunks; kept heads touch one row; every head reads and writes its
+    d-vector state and the emitted row (read again when the L2 flag
+    rescales it)."""
+    d4 = 4.0 * cfg.d_model
+    tot = 0.0
+    for it in batch.items:
+        if it.kind != 0:
+            continue
+        k, l2 = it.pool_kind & ~8, it.pool_kind & 8
+        n = it.n_tokens
+        if k in (0, 1):
+            tot += n * d4 + 2 * d4
+        elif k == 4:
+            tot += 2 * n * d4 + it.ctx_len * d4 * it.is_last
+        else:
+            tot += 2 * d4
+        tot += d4 * it.is_last * (3 if l2 else 1)
+    return tot
 
 
 def kernel_source_digest(name):
@@ -147,7 +172,7 @@ def cpu_baseline(cfg, batch, n_pages, bits, kv_bits):
     from threadpoolctl import threadpool_info
     W = oracle.widen_weights(bits, np.float32)
     K, V = oracle.new_kv(cfg, n_pages, np.float32, kv_bits[0], kv_bits[1])
-    pool = oracle.new_pool(16, cfg.d_model, np.float32)
+    pool = oracle.new_pool(16, cfg.d_model, np.float32, buf_rows=max((it.ctx_len + it.n_tokens for it in batch.items if it.kind == 0), default=0))
     t0 = time.perf_counter()
     oracle.step(cfg, W, batch, (K, V), pool, np.float32)
     dt = time.perf_counter() - t0
@@ -212,6 +237,9 @@ def main():
                     help="one_layer (default line): one Mistral-7B-shaped layer, 4160 rows; mix91/mix55/mix19: "
                          "the 32-layer 9:1 (ten distinct steps), 5:5 (rank 64) and Llama-3.1-8B 1:9 workloads")
     ap.add_argument("--layers", type=int, default=32, help="depth of the mixed workloads")
+    ap.add_argument("--pool-kind", default="last", choices=["last", "mean", "wmean", "cls", "buffer", "last+l2",
+                                                              "mean+l2", "buffer+l2"],
+                    help="pooling head of the one-layer workload's embedding chunks (default: last-token)")
     ap.add_argument("--sampler-only", action="store_true",
                     help="run one step of the workload, then time only the sampler on its logit rows "
                          "(temperature 0.8, top-p 0.9); prints the sampler object")
@@ -244,7 +272,11 @@ def main():
     t_setup = time.time()
     prior_wsum, n_slots = {}, 16
     if args.workload == "one_layer":
-        cfg, batch, n_pages = wl.one_layer_workload()
+        pk_names = {"mean": wl.POOL_MEAN, "wmean": wl.POOL_WMEAN, "cls": wl.POOL_CLS, "last": wl.POOL_LAST,
+                    "buffer": wl.POOL_BUFFER}
+        base, _, l2 = args.pool_kind.partition("+")
+        pool_kind = pk_names[base] | (wl.POOL_L2 if l2 else 0)
+        cfg, batch, n_pages = wl.one_layer_workload(pool_kind=pool_kind)
         batches = [batch]
         bits = sm.make_weights(cfg, seed=0)
         kv_bits = wl.synthetic_kv(cfg, n_pages, seed=3)
@@ -258,8 +290,10 @@ def main():
         kv_bits = None
     max_t = max(b.n_tokens for b in batches)
     max_i = max(b.n_items for b in batches)
+    buf_rows = max((it.ctx_len + it.n_tokens for b in batches for it in b.items
+                    if it.kind == wl.EMBED and (it.pool_kind & ~wl.POOL_L2) == wl.POOL_BUFFER), default=0)
     dev = DeviceModel(cfg, bits, n_pages, max_tokens=max_t, max_items=max_i,
-                      max_pool_slots=n_slots, kv_bits=kv_bits)
+                      max_pool_slots=n_slots, kv_bits=kv_bits, buf_rows=buf_rows)
     if kv_bits is None:
         # prior KV and pooling state of the mixed workloads: SplitMix64 values
         # laid down on the device
@@ -374,7 +408,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.workload],
+        "config": {"workload": (WORKLOAD_TEXT[args.workload] if args.pool_kind == "last" or args.workload != "one_layer"
+                                else WORKLOAD_TEXT[args.workload].replace("last-token pooling",
+                                                                          f"{args.pool_kind} pooling")),
                    "rows": batch.n_tokens, "distinct_steps": len(batches), "embed_rows": meta["n_embed_rows"],
                    "decode_rows": meta["n_decode_rows"], "layers": cfg.n_layers, "d_model": cfg.d_model,
                    "ffn_dim": cfg.ffn_dim, "vocab": cfg.vocab, "lora_rank": cfg.lora_rank},

@@ -198,30 +198,41 @@ __global__ __launch_bounds__(256) void pool_kernel(const float *hf, const int32_
   const int j = blockIdx.y * 256 + lane * 4;  // first of this lane's 4 columns
   const bool cols = j < d;
   if (kind == ORTHRUS_POOL_BUFFER) {
-    // keep this chunk's rows at their positions; on the last chunk run the
-    // head over all N rows: wave w sums rows w, w+4, ... in position order
-    // (rows of this chunk read from hf, which holds the same values), the
-    // waves meet in a fixed order, so the sum order depends on N alone
+    // Keep this chunk's rows at their positions; on the last chunk run the
+    // head over all N rows.  Wave w owns the positions p = w (mod 4) and
+    // sums them in increasing p, buffered rows (p < ctx) first, then this
+    // chunk's rows as it copies them; the waves meet in a fixed order, so
+    // the summation order depends on N alone.
     float *bs = buf + (size_t)slot * buf_rows * d + j;
     const float *hs = hf + (size_t)row0 * d + j;
-    if (cols)
-      for (int r = wave; r < n; r += 4) *(float4 *)(bs + (size_t)(ctx + r) * d) = *(const float4 *)(hs + (size_t)r * d);
-    if (!last) return;
-    const int N = ctx + n;
     float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (cols) {
+      if (last) {
 #pragma unroll 4
-      for (int r = wave; r < N; r += 4) {
-        const float4 v = r < ctx ? *(const float4 *)(bs + (size_t)r * d) : *(const float4 *)(hs + (size_t)(r - ctx) * d);
+        for (int p = wave; p < ctx; p += 4) {
+          const float4 v = *(const float4 *)(bs + (size_t)p * d);
+          s4.x += v.x;
+          s4.y += v.y;
+          s4.z += v.z;
+          s4.w += v.w;
+        }
+      }
+      const int p0 = ctx + ((wave - ctx) & 3);   // first position >= ctx with p = wave (mod 4)
+#pragma unroll 4
+      for (int p = p0; p < ctx + n; p += 4) {
+        const float4 v = *(const float4 *)(hs + (size_t)(p - ctx) * d);
+        *(float4 *)(bs + (size_t)p * d) = v;
         s4.x += v.x;
         s4.y += v.y;
         s4.z += v.z;
         s4.w += v.w;
       }
     }
+    if (!last) return;
     part[wave][lane] = s4;
     __syncthreads();
     if (wave != 0 || !cols) return;
+    const int N = ctx + n;
     const float4 a = part[0][lane], b = part[1][lane], c = part[2][lane], e = part[3][lane];
     const float fN = (float)N;
     float *o = emb + (size_t)out * d + j;
