@@ -81,6 +81,25 @@ def test_sampler_mistral_vocab_many_rows():
     assert np.array_equal(got, ref)
 
 
+def test_sampler_nine_to_one_shape():
+    # the logit rows of the 9:1 step as bench.py times them: 819 rows of the
+    # 32768-token vocabulary, temperature 0.8, top-p 0.9; logits of the spread
+    # the random-weight model produces (standard deviation about 64)
+    rng = np.random.default_rng(21)
+    n, V = 819, 32768
+    print(f"[sample n={n} V={V}]", flush=True)
+    L = (rng.standard_normal((n, V)) * 64).astype(np.float32)
+    temp = np.full(n, 0.8, np.float32)
+    top = np.full(n, 0.9, np.float32)
+    uni = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+    got = _run(L, temp, top, uni)
+    assert np.array_equal(got, oracle_sample(L, temp, top, uni))
+    # and a flatter spread, where the nucleus holds many tokens
+    L = (rng.standard_normal((n, V)) * 1.5).astype(np.float32)
+    got = _run(L, temp, top, uni)
+    assert np.array_equal(got, oracle_sample(L, temp, top, uni))
+
+
 def test_sampler_greedy_and_degenerate():
     rng = np.random.default_rng(13)
     L = rng.standard_normal((5, 777)).astype(np.float32)

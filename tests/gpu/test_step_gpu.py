@@ -99,13 +99,19 @@ def test_random_ragged_batches(seed):
     dev.close()
 
 
-def test_one_mistral_layer_full_batch():
-    cfg, batch, n_pages = wl.one_layer_workload()
-    print(f"one-layer: rows={batch.n_tokens} pages={n_pages}", flush=True)
+@pytest.mark.parametrize("pool_kind", [wl.POOL_LAST, wl.POOL_BUFFER | wl.POOL_L2])
+def test_one_mistral_layer_full_batch(pool_kind):
+    # the one-layer batch as bench.py runs it (default last-token pooling, and
+    # --pool-kind buffer+l2)
+    cfg, batch, n_pages = wl.one_layer_workload(pool_kind=pool_kind)
+    print(f"one-layer: rows={batch.n_tokens} pages={n_pages} pool={pool_kind}", flush=True)
     bits = sm.make_weights(cfg, seed=0)
     kv = wl.synthetic_kv(cfg, n_pages, seed=3)
-    dev, orc = make_pair(cfg, n_pages, bits, kv_bits=kv, max_tokens=8192, max_items=128)
-    run_and_compare(cfg, dev, orc, batch, tag="one-layer")
+    buf = 512 if (pool_kind & ~wl.POOL_L2) == wl.POOL_BUFFER else 0
+    dev, orc = make_pair(cfg, n_pages, bits, kv_bits=kv, max_tokens=8192, max_items=128, buf_rows=buf)
+    got, _, _ = run_and_compare(cfg, dev, orc, batch, tag="one-layer")
+    if pool_kind & wl.POOL_L2:
+        assert np.allclose(np.linalg.norm(got["emb"].astype(np.float64), axis=1), 1.0, atol=1e-5)
     dev.close()
 
 
