@@ -16,6 +16,8 @@
 #include "device_common.h"
 #include "orthrus_internal.h"
 
+#include <type_traits>
+
 namespace orthrus {
 
 struct GemmArgs {
@@ -152,8 +154,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     }
   };
   // all k slices of one stage; fragments of slice k+1 are read before the
-  // MFMAs of slice k are issued so LDS latency hides behind matrix work
-  auto compute = [&](int st) {
+  // MFMAs of slice k are issued so LDS latency hides behind matrix work.
+  // `loads` issues the global loads of a later K-step; they are placed one
+  // after each of the first MFMAs of slice 0, so the waves of a SIMD, which
+  // leave the step's barrier together, keep the matrix pipe busy while the
+  // loads go out.
+  auto compute = [&](int st, auto &&loads) {
     const uint16_t *As = As0 + st * BM * BK, *Bs = Bs0 + st * BNB * BK;
     bf16x8_t a[2][MI], b[2][NI];
     load_frags(As, Bs, 0, a[0], b[0]);
@@ -166,6 +172,14 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NI; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
+      if (kk == 0) {
+        loads();
+#pragma unroll
+        for (int q = 0; q < LPT; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one VMEM
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -208,21 +222,34 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
         boff[i] = ncol < g.N ? (uint32_t)(((size_t)ncol * g.r + kc * 8 - sec * g.r) * 2) : OOB;
       }
     }
-    auto issue = [&](int kt) {
+    // FULL: all BK columns of the step lie inside the main operands, so
+    // only the row check (already folded into the offset) remains
+    auto issue = [&](int kt, auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
       const int k0 = kt * BK, st = kt % S;
 #pragma unroll
       for (int i = 0; i < A_ROUNDS; ++i) {
-        const bool ok = (k0 + akc[i]) < Kp && aoff[i] != OOB;
-        const uint32_t off = ok ? aoff[i] + (uint32_t)(k0 * 2) : OOB;
+        uint32_t off;
+        if (FULL) {
+          off = aoff[i] + (uint32_t)(k0 * 2);  // OOB + k0*2 stays out of range
+        } else {
+          const bool ok = (k0 + akc[i]) < Kp && aoff[i] != OOB;
+          off = ok ? aoff[i] + (uint32_t)(k0 * 2) : OOB;
+        }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, (lds_ptr_t)(As0 + st * BM * BK + (i * NW + wave) * 512), 16, off, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < B_ROUNDS; ++i) {
-        bool ok = boff[i] != OOB;
-        if (phase == 0) ok = ok && (k0 + bkc[i]) < Kp;
-        else ok = ok && (k0 + bkc[i]) >= 0 && (k0 + bkc[i]) < g.r;
-        const uint32_t off = ok ? boff[i] + (uint32_t)(k0 * 2) : OOB;
+        uint32_t off;
+        if (FULL && phase == 0) {
+          off = boff[i] + (uint32_t)(k0 * 2);
+        } else {
+          bool ok = boff[i] != OOB;
+          if (phase == 0) ok = ok && (k0 + bkc[i]) < Kp;
+          else ok = ok && (k0 + bkc[i]) >= 0 && (k0 + bkc[i]) < g.r;
+          off = ok ? boff[i] + (uint32_t)(k0 * 2) : OOB;
+        }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rb, (lds_ptr_t)(Bs0 + st * BNB * BK + (i * NW + wave) * 512), 16, off, 0, 0, 0);
       }
@@ -231,15 +258,29 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     // flight while step kt is consumed; one barrier per step both publishes
     // step kt and retires the stage that the next issue overwrites.  The
     // bare s_barrier avoids the fence of __syncthreads, which would drain
-    // the loads in flight.
+    // the loads in flight.  The loop is split so that each part is one
+    // straight-line block (the loads can then be scheduled among the
+    // MFMAs): steps that load a full K-step, steps that load a ragged or
+    // adapter step, and the last S-1 steps, which load nothing.
 #pragma unroll
     for (int p = 0; p < S - 1; ++p)
-      if (kb + p < ke) issue(kb + p);
-    for (int kt = kb; kt < ke; ++kt) {
+      if (kb + p < ke) issue(kb + p, std::false_type{});
+    const int nfull = phase == 0 ? Kp / BK : 0;
+    int kt = kb;
+    for (; kt + S - 1 < ke && kt + S - 1 < nfull; ++kt) {
+      wait_tiles<LPT, S>(S - 2);
+      __builtin_amdgcn_s_barrier();
+      compute(kt % S, [&] { issue(kt + S - 1, std::true_type{}); });
+    }
+    for (; kt + S - 1 < ke; ++kt) {
+      wait_tiles<LPT, S>(S - 2);
+      __builtin_amdgcn_s_barrier();
+      compute(kt % S, [&] { issue(kt + S - 1, std::false_type{}); });
+    }
+    for (; kt < ke; ++kt) {
       wait_tiles<LPT, S>(min(S - 2, ke - 1 - kt));
       __builtin_amdgcn_s_barrier();
-      if (kt + S - 1 < ke) issue(kt + S - 1);
-      compute(kt % S);
+      compute(kt % S, [] {});
     }
   };
 
@@ -267,12 +308,45 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     if (m < g.M) c[0] = (uint16_t)(w & 0xffffu);
     if (m + 1 < g.M) c[g.ldc] = (uint16_t)(w >> 16);
   };
-  auto epilogue = [&]() {
+  // whole: this workgroup ran every K-step of the tile, so a residual
+  // output is a plain read-modify-write of x (its loads batched per 32-row
+  // block); stream-K slices of a tile add theirs with float atomics
+  auto epilogue = [&](const bool whole) {
     const int jc = lane & 31;
     const int rbase = (lane >> 5) * 4;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      if (DUAL) {
+      if (EPI == EPI_RESID && whole) {
+        // 32-bit buffer offsets; rows past M or columns past N get an
+        // out-of-range offset, which loads as zero and is not stored.  The
+        // x values of the next 32x32 block are loaded before the current
+        // block is stored.
+        if (i > 0) continue;  // all blocks of the wave tile are handled at i == 0
+        const __amdgpu_buffer_rsrc_t rx =
+            __builtin_amdgcn_make_buffer_rsrc(g.C, (short)0, (int)0x7fffffff, 0x00020000);
+        auto xoff = [&](int blk, int e) -> uint32_t {
+          const int n = n0 + wn * WCN + (blk % NI) * 32 + jc;
+          const int m = m0 + wm * WTM + (blk / NI) * 32 + rbase + (e / 4) * 8 + (e % 4);
+          return (m < g.M && n < g.N) ? (uint32_t)((m * g.ldc + n) * 4) : OOB;
+        };
+        uint32_t xv[2][16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xv[0][e] = __builtin_amdgcn_raw_buffer_load_b32(rx, xoff(0, e), 0, 0);
+#pragma unroll
+        for (int blk = 0; blk < MI * NI; ++blk) {
+          if (blk + 1 < MI * NI) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              xv[(blk + 1) & 1][e] = __builtin_amdgcn_raw_buffer_load_b32(rx, xoff(blk + 1, e), 0, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float v = __uint_as_float(xv[blk & 1][e]) + acc[blk / NI][blk % NI][e];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rx, xoff(blk, e), 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else if (DUAL) {
         // silu(g) u = g u / (1 + 2^(-g log2 e)): v_exp_f32 and v_rcp_f32
 #pragma unroll
         for (int j = 0; j < NI / 2; ++j) {
@@ -310,7 +384,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
               const size_t o = (size_t)m * g.ldc + n;
               const float v = acc[i][j][e];
               if (EPI == EPI_F32) ((float *)g.C)[o] = g.alpha * v;
-              else unsafeAtomicAdd((float *)g.C + o, v);  // residual: x += v
+              else unsafeAtomicAdd((float *)g.C + o, v);  // stream-K slice: x += v
             }
           }
         }
@@ -326,16 +400,17 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
       __builtin_amdgcn_s_barrier();  // all waves are done with the last stage
       run_phase(1, g.ldu, 0, (g.ldu + BK - 1) / BK);
     }
-    epilogue();
+    epilogue(true);
   } else if (EPI == EPI_RESID) {
     // residual projections on a grid of sk_grid workgroups (one per CU):
-    // whole tiles first, q consecutive tiles of the grouped order per
-    // workgroup, then the tiles left over shared out as equal slices of
-    // their K-steps (stream-K)
+    // whole tiles first, in rounds of sk_grid consecutive tiles of the
+    // grouped order (so the tiles in flight at once are neighbours), then
+    // the tiles left over shared out as equal slices of their K-steps
+    // (stream-K)
     const int w = xcd_remap(blockIdx.x, g.sk_grid);
     const int q = P / g.sk_grid;
     const int P_dp = q * g.sk_grid;
-    for (int t = w * q; t < (w + 1) * q; ++t) {
+    for (int t = w; t < P_dp; t += g.sk_grid) {
       set_tile(t);
       zero_acc();
       __builtin_amdgcn_s_barrier();  // the previous tile's stages are retired
@@ -344,7 +419,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
         __builtin_amdgcn_s_barrier();
         run_phase(1, g.ldu, 0, (g.ldu + BK - 1) / BK);
       }
-      epilogue();
+      epilogue(true);
     }
     const long total = (long)(P - P_dp) * nk;
     long it = total * w / g.sk_grid;
@@ -361,7 +436,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
         __builtin_amdgcn_s_barrier();
         run_phase(1, g.ldu, 0, (g.ldu + BK - 1) / BK);
       }
-      epilogue();
+      epilogue(kb == 0 && ke == nk);
       it += ke - kb;
     }
   }
@@ -432,9 +507,15 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
       if (big) return launch_cfg<256, 256, 2, 4, 64, 2, EPI_F32>(a, s);
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_F32>(a, s);
     case EPI_RESID:
-      // residual projections have few output tiles (N = d): one workgroup
-      // per CU, whole tiles in L2-friendly order, the remainder stream-K
-      if (big) return launch_cfg<256, 256, 4, 2, 64, 2, EPI_RESID>(a, s, cu_count());
+      // residual projections have few output tiles (N = d).  When the tiles
+      // past the last full round would leave most CUs idle, one workgroup
+      // per CU runs the whole tiles and shares the rest out stream-K;
+      // otherwise one workgroup per tile (measured faster at 512 tiles).
+      if (big) {
+        const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+        const int rem = tiles % cu_count();
+        return launch_cfg<256, 256, 4, 2, 64, 2, EPI_RESID>(a, s, rem != 0 && rem < cu_count() / 2 ? cu_count() : 0);
+      }
       if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_RESID>(a, s);
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);
     case EPI_SWIGLU:

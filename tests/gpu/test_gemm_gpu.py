@@ -26,7 +26,13 @@ def _rel(a, b):
 
 SHAPES = [(34, 128, 64), (300, 176, 64), (129, 257, 176), (1, 64, 4096), (4160, 384, 512),
           (64, 1000, 4096), (1040, 2056, 520), (700, 1300, 200), (512, 1024, 64),
-          (2000, 1536, 2048)]
+          (2000, 1536, 2048),
+          # residual grid of one workgroup per CU: 256 whole tiles (plain
+          # read-modify-write) plus a stream-K remainder, ragged rows and columns
+          (4160, 4096, 256), (4100, 4200, 128),
+          # residual grid of one workgroup per tile (the tiles past the last
+          # full round of CUs fill at least half of them)
+          (2048, 4096, 64), (1800, 4100, 72)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
