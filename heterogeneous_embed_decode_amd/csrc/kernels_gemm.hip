@@ -38,6 +38,15 @@ struct GemmArgs {
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
+// MFMA block size: 32 selects v_mfma_f32_32x32x16_bf16, 16 selects
+// v_mfma_f32_16x16x32_bf16.  Both have the same peak rate.  In a
+// register-only MFMA loop on MI355X with random bf16 operands the 16x16 form
+// sustained 80-82 % of the bf16 peak against 65-73 % for the 32x32 form
+// (with zero operands both reach about 98 %: the chip is power-limited),
+// but in this kernel both forms ran within 1 % of each other, and the 16x16
+// form needs more registers for its 32-deep fragments, so 32 is used.
+constexpr int MT = 32;
+
 // LDS swizzle of the 16-byte chunks of one tile row (BK/8 chunks).
 // ds_read_b128 is served 16 lanes at a time across 64 banks (256 bytes);
 // the 16 rows a half-wave reads must land on 16 distinct 16-byte bank
@@ -71,8 +80,11 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BNB = DUAL ? 2 * BN : BN;      // B rows staged per tile
   constexpr int WTM = BM / WM;                  // wave tile rows
   constexpr int WCN = BN / WN;                  // wave tile output columns
-  constexpr int MI = WTM / 32;
-  constexpr int NI = DUAL ? 2 * (WCN / 32) : WCN / 32;
+  constexpr int MI = WTM / MT;                  // MFMA blocks per wave tile
+  constexpr int NI = DUAL ? 2 * (WCN / MT) : WCN / MT;
+  constexpr int KS = MT == 32 ? 16 : 32;        // k per MFMA
+  constexpr int NE = MT == 32 ? 16 : 4;         // accumulators per lane per block
+  using acc_t = typename std::conditional<MT == 32, f32x16_t, f32x4_t>::type;
   constexpr int CPR = BK / 8;                   // 16-byte chunks per tile row
   constexpr int RPI = 64 / CPR;                 // tile rows per wave load instruction
   constexpr int A_ROUNDS = BM / (RPI * NW);
@@ -113,7 +125,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     return b < per * 8 ? (b % 8) * per + b / 8 : b;
   };
 
-  f32x16_t acc[MI][NI];
+  acc_t acc[MI][NI];
 
   // B tile row rr -> output column of that row and its global B row
   auto b_src_row = [&](int rr, int &ncol) -> int {
@@ -135,21 +147,22 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr uint32_t OOB = 0x80000000u;
   const int lrow = lane / CPR, pc = lane % CPR;
 
-  // MFMA operand fragments of one 16-wide k slice
+  // MFMA operand fragments of one KS-wide k slice: lane l holds row (or
+  // column) l % MT and the 8 consecutive k of chunk l / MT of the slice
   auto load_frags = [&](const uint16_t *As, const uint16_t *Bs, int kk, bf16x8_t *a, bf16x8_t *b) {
-    const int chunk = kk * 2 + (lane >> 5);
+    const int chunk = kk * (KS / 8) + lane / MT;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int row = wm * WTM + i * 32 + (lane & 31);
+      const int row = wm * WTM + i * MT + (lane & (MT - 1));
       a[i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(&As[row * BK + ((chunk ^ swz<BK>(row)) * 8)]));
     }
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       int rr;
       if (DUAL)
-        rr = (j < NI / 2 ? 0 : BN) + wn * WCN + (j % (NI / 2)) * 32 + (lane & 31);
+        rr = (j < NI / 2 ? 0 : BN) + wn * WCN + (j % (NI / 2)) * MT + (lane & (MT - 1));
       else
-        rr = wn * WCN + j * 32 + (lane & 31);
+        rr = wn * WCN + j * MT + (lane & (MT - 1));
       b[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(&Bs[rr * BK + ((chunk ^ swz<BK>(rr)) * 8)]));
     }
   };
@@ -164,14 +177,18 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     bf16x8_t a[2][MI], b[2][NI];
     load_frags(As, Bs, 0, a[0], b[0]);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+    for (int kk = 0; kk < BK / KS; ++kk) {
+      if (kk + 1 < BK / KS) load_frags(As, Bs, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NI; ++j) {
+          if constexpr (MT == 32)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
+        }
       if (kk == 0) {
         loads();
 #pragma unroll
@@ -290,12 +307,14 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < NI; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        for (int e = 0; e < NE; ++e) acc[i][j][e] = 0.f;
   };
 
   const int nk = (g.K + BK - 1) / BK;
   const bool lora_tile_possible = !DUAL && g.U != nullptr;
-  // epilogue: lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane/32) + e%4
+  // epilogue: in each MT x MT block the lane holds column lane % MT and
+  // rows erow(e): 8*(e/4) + 4*(lane/32) + e%4 for MT = 32, 4*(lane/16) + e
+  // for MT = 16 (rows e and e+1 are adjacent for even e in both)
   // residual: hardware float atomic add into x (no return value to wait
   // for); stream-K partial sums of one tile land in no fixed order
   // bf16 outputs: two rows (e, e+1) of the lane's column are converted by
@@ -312,49 +331,55 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   // output is a plain read-modify-write of x (its loads batched per 32-row
   // block); stream-K slices of a tile add theirs with float atomics
   auto epilogue = [&](const bool whole) {
-    const int jc = lane & 31;
-    const int rbase = (lane >> 5) * 4;
+    const int jc = lane & (MT - 1);
+    auto erow = [&](int e) { return MT == 32 ? (e / 4) * 8 + (lane >> 5) * 4 + (e % 4) : (lane >> 4) * 4 + e; };
+    const int mw = m0 + wm * WTM, nw = n0 + wn * WCN;
+    if (EPI == EPI_RESID && whole) {
+      // 32-bit buffer offsets; rows past M or columns past N get an
+      // out-of-range offset, which loads as zero and is not stored.  The
+      // lane's values are taken in groups of 16; the x values of the next
+      // group are loaded before the current group is stored.
+      const __amdgpu_buffer_rsrc_t rx =
+          __builtin_amdgcn_make_buffer_rsrc(g.C, (short)0, (int)0x7fffffff, 0x00020000);
+      constexpr int NV = MI * NI * NE, NG = NV / 16;
+      static_assert(NV % 16 == 0, "whole groups of 16 values");
+      auto xoff = [&](int v) -> uint32_t {
+        const int blk = v / NE, e = v % NE;
+        const int n = nw + (blk % NI) * MT + jc;
+        const int m = mw + (blk / NI) * MT + erow(e);
+        return (m < g.M && n < g.N) ? (uint32_t)((m * g.ldc + n) * 4) : OOB;
+      };
+      uint32_t xv[2][16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) xv[0][u] = __builtin_amdgcn_raw_buffer_load_b32(rx, xoff(u), 0, 0);
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        if (gi + 1 < NG) {
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            xv[(gi + 1) & 1][u] = __builtin_amdgcn_raw_buffer_load_b32(rx, xoff((gi + 1) * 16 + u), 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int v = gi * 16 + u, blk = v / NE;
+          const float r = __uint_as_float(xv[gi & 1][u]) + acc[blk / NI][blk % NI][v % NE];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r), rx, xoff(v), 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      if (EPI == EPI_RESID && whole) {
-        // 32-bit buffer offsets; rows past M or columns past N get an
-        // out-of-range offset, which loads as zero and is not stored.  The
-        // x values of the next 32x32 block are loaded before the current
-        // block is stored.
-        if (i > 0) continue;  // all blocks of the wave tile are handled at i == 0
-        const __amdgpu_buffer_rsrc_t rx =
-            __builtin_amdgcn_make_buffer_rsrc(g.C, (short)0, (int)0x7fffffff, 0x00020000);
-        auto xoff = [&](int blk, int e) -> uint32_t {
-          const int n = n0 + wn * WCN + (blk % NI) * 32 + jc;
-          const int m = m0 + wm * WTM + (blk / NI) * 32 + rbase + (e / 4) * 8 + (e % 4);
-          return (m < g.M && n < g.N) ? (uint32_t)((m * g.ldc + n) * 4) : OOB;
-        };
-        uint32_t xv[2][16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) xv[0][e] = __builtin_amdgcn_raw_buffer_load_b32(rx, xoff(0, e), 0, 0);
-#pragma unroll
-        for (int blk = 0; blk < MI * NI; ++blk) {
-          if (blk + 1 < MI * NI) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-              xv[(blk + 1) & 1][e] = __builtin_amdgcn_raw_buffer_load_b32(rx, xoff(blk + 1, e), 0, 0);
-          }
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float v = __uint_as_float(xv[blk & 1][e]) + acc[blk / NI][blk % NI][e];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rx, xoff(blk, e), 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else if (DUAL) {
+      if (DUAL) {
         // silu(g) u = g u / (1 + 2^(-g log2 e)): v_exp_f32 and v_rcp_f32
 #pragma unroll
         for (int j = 0; j < NI / 2; ++j) {
-          const int n = n0 + wn * WCN + j * 32 + jc;
+          const int n = nw + j * MT + jc;
           if (n >= g.N) continue;
 #pragma unroll
-          for (int e = 0; e < 16; e += 2) {
-            const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
+          for (int e = 0; e < NE; e += 2) {
+            const int m = mw + i * MT + erow(e);
             float o2[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -368,18 +393,18 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
       } else {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-          const int n = n0 + wn * WCN + j * 32 + jc;
+          const int n = nw + j * MT + jc;
           if (n >= g.N) continue;
           if (EPI == EPI_BF16) {
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-              const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
+            for (int e = 0; e < NE; e += 2) {
+              const int m = mw + i * MT + erow(e);
               store_bf16_pair(m, n, g.alpha * acc[i][j][e], g.alpha * acc[i][j][e + 1]);
             }
           } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + rbase + (e % 4);
+            for (int e = 0; e < NE; ++e) {
+              const int m = mw + i * MT + erow(e);
               if (m >= g.M) continue;
               const size_t o = (size_t)m * g.ldc + n;
               const float v = acc[i][j][e];
