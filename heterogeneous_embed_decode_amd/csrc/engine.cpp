@@ -50,6 +50,10 @@ struct orthrus_engine {
 
 namespace {
 
+// a byte extent the 32-bit buffer offsets of the GEMM kernels can address
+// (the buffer resources cover 0x7fffffff bytes)
+bool fits_buffer(size_t bytes) { return bytes < 0x7fffffffu; }
+
 orthrus_status hip_fail(orthrus_engine *e, hipError_t r, const char *what) {
   if (e) e->err = std::string(what) + ": " + hipGetErrorString(r);
   return ORTHRUS_EHIP;
@@ -188,6 +192,15 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) return ORTHRUS_EINVAL;
   if (c.d_model % 8 || c.ffn_dim % 8 || c.lora_rank % 8 || c.d_model > 8192 || c.lora_rank > 64)
     return ORTHRUS_EINVAL;
+  {
+    // GEMM operands and the fp32 residual are addressed through 32-bit
+    // buffer offsets: every row-major operand of a step must stay below 2 GiB
+    const size_t qkv_w = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * hd;
+    const size_t widest = std::max({(size_t)c.d_model, qkv_w, (size_t)c.ffn_dim});
+    if (!fits_buffer((size_t)c.max_tokens * widest * 4) || !fits_buffer((size_t)c.vocab * c.d_model * 2) ||
+        !fits_buffer((size_t)2 * c.ffn_dim * c.d_model * 2) || !fits_buffer(qkv_w * c.d_model * 2))
+      return ORTHRUS_EINVAL;
+  }
   for (int l = 0; l < c.n_layers; ++l) {
     const orthrus_layer_w &L = w->layers[l];
     if (!L.w_qkv || !L.w_o || !L.w_gate_up || !L.w_down || !L.g_attn || !L.g_ffn) return ORTHRUS_EINVAL;
@@ -512,6 +525,13 @@ orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int3
       epilogue < 0 || epilogue > 3 || ldc < N)
     return ORTHRUS_EINVAL;
   if (epilogue == EPI_SWIGLU && b_up_row < N) return ORTHRUS_EINVAL;
+  // the kernels address A, B and a residual C through 32-bit buffer offsets
+  if (M > 0 && N > 0) {
+    const size_t b_rows = epilogue == EPI_SWIGLU ? (size_t)b_up_row + N : (size_t)N;
+    if (!fits_buffer(((size_t)(M - 1) * lda + K) * 2) || !fits_buffer(((b_rows - 1) * ldb + K) * 2) ||
+        (epilogue == EPI_RESID && !fits_buffer(((size_t)(M - 1) * ldc + N) * 4)))
+      return ORTHRUS_EINVAL;
+  }
   const int r = launch_gemm((const uint16_t *)A, lda, (const uint16_t *)B, ldb, C, ldc, M, N, K, epilogue,
                             b_up_row, 1.f, nullptr, stream);
   return r ? ORTHRUS_EHIP : ORTHRUS_OK;

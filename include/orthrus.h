@@ -162,9 +162,11 @@ orthrus_status orthrus_pack(const orthrus_model_cfg *cfg, const orthrus_batch *b
  * k_pages / v_pages: device bf16 KV pools (layout above), read and written
  * by every step.  Returns EINVAL for unsupported shapes (head_dim not in
  * {16,32,64,128}, n_q_heads not a multiple of n_kv_heads, d_model above
- * 8192, d_model, Hq*hd,
- * ffn_dim not multiples of 8, lora_rank not a multiple of 8), ENOMEM or
- * EHIP on allocation failure. */
+ * 8192, d_model, Hq*hd, ffn_dim not multiples of 8, lora_rank not a
+ * multiple of 8, or a step operand of 2 GiB or more: max_tokens rows of
+ * the widest activation in fp32, or the vocab x d_model, 2 ffn_dim x
+ * d_model or (Hq + 2 Hkv) hd x d_model weight in bf16), ENOMEM or EHIP on
+ * allocation failure. */
 orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weights *w,
                               void *k_pages, void *v_pages, orthrus_engine **out);
 
@@ -227,13 +229,17 @@ orthrus_status orthrus_fill_hash_bf16(void *dst, uint64_t n, uint32_t seed, uint
 /* Standalone bf16 GEMM on the MFMA kernels of the step (device pointers):
  *   C = A B^T with A [M][K] (lda), B [N][K] (ldb), fp32 accumulation.
  * epilogue: 0 store C as bf16 [M][N] (ldc); 1 store fp32; 2 fp32 C += A B^T
- *             by float atomic adds (large problems split K over workgroups,
- *             so the partial sums land in no fixed order);
+ *             (a tile that one workgroup computes over all of K is read,
+ *             added and written; where large problems split K over
+ *             workgroups, the partial sums land by float atomic adds in
+ *             no fixed order, so C must not be read or written by other
+ *             work on the device meanwhile);
  *           3 SwiGLU: B holds 2N rows at ldb (gate rows 0..N-1, up rows
  *             N..2N-1 at row offset b_up_row), C bf16 = silu(gate) * up.
- * K must be a multiple of 8.  Returns EINVAL for bad sizes, EHIP on
- * launch failure.  Used by the step for the projections of the forward
- * pass (§3.1: attention and feed-forward layers are shared by all items). */
+ * K must be a multiple of 8.  A, B and (epilogue 2) C are addressed
+ * through 32-bit buffer offsets, so each must span less than 2 GiB.
+ * Returns EINVAL for bad sizes, EHIP on launch failure.  Used by the step
+ * for the projections of the forward pass (§3.1: attention and feed-forward layers are shared by all items). */
 orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int32_t ldb,
                                  void *C, int32_t ldc, int32_t M, int32_t N, int32_t K,
                                  int32_t epilogue, int32_t b_up_row, void *stream);

@@ -134,3 +134,14 @@ def test_capacity_of_pack_outputs():
     st = hed.LIB.orthrus_pack(ctypes.byref(cfg_for(sm.TINY, 8)), ctypes.byref(ba.struct),
                               ctypes.byref(pk), None, 0)
     assert st == hed.ECAPACITY
+
+
+def test_gemm_rejects_operands_of_2gib():
+    """The GEMM kernels address A, B and a residual C through 32-bit buffer
+    offsets; an operand spanning 2 GiB is refused before any device work
+    (the pointers are never dereferenced)."""
+    big = 1 << 17   # rows: 131072 x 8192 bf16 = 2 GiB
+    assert hed.orthrus_gemm_bf16(8, 8192, 8, 8192, 8, 64, big, 64, 8192, hed.EPI_BF16) == hed.EINVAL
+    assert hed.orthrus_gemm_bf16(8, 8192, 8, 8192, 8, big, 64, big, 8192, hed.EPI_BF16) == hed.EINVAL
+    # residual C: 65536 x 8192 fp32 = 2 GiB (A and B are small)
+    assert hed.orthrus_gemm_bf16(8, 64, 8, 64, 8, 8192, 65536, 8192, 64, hed.EPI_RESID) == hed.EINVAL
