@@ -544,7 +544,25 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
       if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_RESID>(a, s);
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);
     case EPI_SWIGLU:
-      if (big) return launch_cfg<256, 128, 2, 4, 64, 2, EPI_SWIGLU>(a, s);
+      if (big) {
+        // a last tile row of at most 64 rows costs a whole extra round of
+        // 256-row tiles when the full tile rows fill whole rounds; those
+        // rows then go to a launch of 64-row tiles instead
+        const int tn = (N + 127) / 128, full = M / 256, rest = M - full * 256;
+        const int cus = cu_count();
+        if (rest > 0 && rest <= 64 && full > 0 &&
+            (full * tn + cus - 1) / cus < ((full + 1) * tn + cus - 1) / cus) {
+          GemmArgs lo = a;
+          lo.M = full * 256;
+          if (int r = launch_cfg<256, 128, 2, 4, 64, 2, EPI_SWIGLU>(lo, s)) return r;
+          GemmArgs hi = a;
+          hi.A = A + (size_t)lo.M * lda;
+          hi.C = (uint16_t *)C + (size_t)lo.M * ldc;
+          hi.M = rest;
+          return launch_cfg<64, 64, 2, 2, 64, 4, EPI_SWIGLU>(hi, s);
+        }
+        return launch_cfg<256, 128, 2, 4, 64, 2, EPI_SWIGLU>(a, s);
+      }
       if (skinny) return launch_cfg<64, 64, 2, 2, 64, 4, EPI_SWIGLU>(a, s);
       return launch_cfg<128, 64, 2, 2, 64, 2, EPI_SWIGLU>(a, s);
   }

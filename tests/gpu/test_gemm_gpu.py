@@ -65,7 +65,9 @@ def test_gemm_epilogues(M, N, K, epi):
     assert _rel(got, ref) < tol
 
 
-@pytest.mark.parametrize("M,F,K", [(34, 176, 64), (257, 200, 128), (1024, 1024, 512), (777, 1160, 264)])
+@pytest.mark.parametrize("M,F,K", [(34, 176, 64), (257, 200, 128), (1024, 1024, 512), (777, 1160, 264),
+                                   # a last tile row of 64 or fewer rows run as a launch of 64-row tiles
+                                   (4160, 2048, 256), (2112, 4096, 128), (1040, 8192, 64)])
 def test_gemm_swiglu(M, F, K):
     print(f"swiglu M={M} F={F} K={K}", flush=True)
     rng = np.random.default_rng(M + F)
