@@ -321,8 +321,40 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   HIPCHK(hipSetDevice(eng->device), "hipSetDevice");
   hipStream_t s = (hipStream_t)stream;
 
-  // metadata block (int32 words, 16-byte aligned sections)
+  // embedding rows the pooling heads read from the final norm: every row
+  // of a mean, weighted-mean or buffered segment, the first row of a CLS
+  // segment that starts its request, the last row of a LAST segment
+  // (norm_subset false: all embedding rows, in order)
   const size_t n_segs = p.pool_segs.size() / 8;
+  std::vector<int32_t> norm_rows;
+  bool norm_subset = false;
+  {
+    size_t need = 0;
+    for (size_t q = 0; q < n_segs; ++q) {
+      const int32_t *sg = &p.pool_segs[q * 8];
+      const int kind = sg[3] & ~ORTHRUS_POOL_L2;
+      if (kind == ORTHRUS_POOL_CLS) need += sg[4] ? 1 : 0;
+      else if (kind == ORTHRUS_POOL_LAST) need += 1;
+      else need += sg[1];
+    }
+    if (need < (size_t)p.rows_by_kind[0]) {
+      norm_subset = true;
+      norm_rows.reserve(need);
+      for (size_t q = 0; q < n_segs; ++q) {
+        const int32_t *sg = &p.pool_segs[q * 8];
+        const int kind = sg[3] & ~ORTHRUS_POOL_L2;
+        if (kind == ORTHRUS_POOL_CLS) {
+          if (sg[4]) norm_rows.push_back(sg[0]);
+        } else if (kind == ORTHRUS_POOL_LAST) {
+          norm_rows.push_back(sg[0] + sg[1] - 1);
+        } else {
+          for (int r = 0; r < sg[1]; ++r) norm_rows.push_back(sg[0] + r);
+        }
+      }
+    }
+  }
+
+  // metadata block (int32 words, 16-byte aligned sections)
   size_t off = 0;
   const size_t o_tok = off; off = align4(off + T);
   const size_t o_pos = off; off = align4(off + T);
@@ -333,6 +365,7 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   const size_t o_dec = off; off = align4(off + dec_items.size());
   const size_t o_items = off; off = align4(off + eng->items.size() * 8);
   const size_t o_work = off; off = align4(off + eng->work.size() * 8);
+  const size_t o_norm = off; off = align4(off + norm_rows.size());
   const size_t words = std::max<size_t>(off, 4);
   if (eng->staged_pending) {
     HIPCHK(hipEventSynchronize(eng->staged), "hipEventSynchronize");
@@ -380,6 +413,7 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   if (!dec_items.empty()) memcpy(mh + o_dec, dec_items.data(), dec_items.size() * 4);
   if (!eng->items.empty()) memcpy(mh + o_items, eng->items.data(), eng->items.size() * 32);
   if (!eng->work.empty()) memcpy(mh + o_work, eng->work.data(), eng->work.size() * 32);
+  if (!norm_rows.empty()) memcpy(mh + o_norm, norm_rows.data(), norm_rows.size() * 4);
   HIPCHK(hipMemcpyAsync(eng->meta_dev, mh, words * 4, hipMemcpyHostToDevice, s), "metadata upload");
   HIPCHK(hipEventRecord(eng->staged, s), "hipEventRecord");
   eng->staged_pending = true;
@@ -448,8 +482,9 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   }
   if (hidden_out)
     HIPCHK(hipMemcpyAsync(hidden_out, eng->x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s), "hidden copy");
-  LCHK(launch_final_norm(eng->x, (const uint16_t *)eng->w.g_final, d_logit, TE, G, eng->hf, eng->hl, d,
-                         c.rms_eps, s),
+  LCHK(launch_final_norm(eng->x, (const uint16_t *)eng->w.g_final, d_logit,
+                         norm_subset ? eng->meta_dev + o_norm : nullptr,
+                         norm_subset ? (int)norm_rows.size() : TE, G, eng->hf, eng->hl, d, c.rms_eps, s),
        "final_norm");
   if (G > 0)
     LCHK(launch_gemm(eng->hl, d, (const uint16_t *)eng->w.lm_head, d, logits, c.vocab, G, c.vocab, d, EPI_F32,

@@ -142,15 +142,16 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(uint16_t *qkv, const int32
 }
 
 // Final RMSNorm for the rows the outputs need: blocks [0, n_embed) normalise
-// embedding rows into hf (fp32, pooler input); blocks [n_embed, n_embed +
-// n_logit) normalise logit_rows[] into hl (bf16, LM-head input).
+// embedding rows (emb_rows[b], or row b when emb_rows is null) into hf at
+// their row (fp32, pooler input); blocks [n_embed, n_embed + n_logit)
+// normalise logit_rows[] into hl (bf16, LM-head input).
 __global__ __launch_bounds__(256) void final_norm_kernel(const float *x, const uint16_t *g,
-                                                         const int32_t *logit_rows, int n_embed,
-                                                         float *hf, uint16_t *hl, int d, float eps) {
+                                                         const int32_t *logit_rows, const int32_t *emb_rows,
+                                                         int n_embed, float *hf, uint16_t *hl, int d, float eps) {
   __shared__ float red[4];
   const int b = blockIdx.x;
   const bool emb = b < n_embed;
-  const int row = emb ? b : logit_rows[b - n_embed];
+  const int row = emb ? (emb_rows ? emb_rows[b] : b) : logit_rows[b - n_embed];
   const float *xr = x + (size_t)row * d;
   const int nv4 = d / 4;
   float4 v[NORM_MAXV];
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float *x, const u
     const int c = threadIdx.x + j * 256;
     if (c >= nv4) break;
     const uint2 gw = *(const uint2 *)(g + c * 4);
-    *(float4 *)(hf + (size_t)b * d + c * 4) =
+    *(float4 *)(hf + (size_t)row * d + c * 4) =
         make_float4(v[j].x * inv * lo_bf(gw.x), v[j].y * inv * hi_bf(gw.x), v[j].z * inv * lo_bf(gw.y),
                     v[j].w * inv * hi_bf(gw.y));
   }
@@ -350,11 +351,11 @@ int launch_rope_kv(uint16_t *qkv, const int32_t *pos, const int32_t *slot, const
   return 0;
 }
 
-int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_rows, int n_embed,
-                      int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream) {
+int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_rows, const int32_t *emb_rows,
+                      int n_embed, int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream) {
   if (n_embed + n_logit <= 0) return 0;
   hipLaunchKernelGGL(final_norm_kernel, dim3(n_embed + n_logit), dim3(256), 0, (hipStream_t)stream, x,
-                     g, logit_rows, n_embed, hf, hl, d, eps);
+                     g, logit_rows, emb_rows, n_embed, hf, hl, d, eps);
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }

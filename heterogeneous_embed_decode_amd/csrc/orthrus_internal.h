@@ -82,8 +82,8 @@ int launch_attn_decode(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, cons
 int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_dec,
                         const float *part_ml, const float *part_o, uint16_t *o, int ld_o,
                         int Hq, int Hkv, int hd, void *stream);
-int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_rows, int n_embed,
-                      int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream);
+int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_rows, const int32_t *emb_rows,
+                      int n_embed, int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream);
 int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, int nr, int K, float scale,
                        uint16_t *U, void *stream);
 int launch_sample(const float *logits, int64_t ld, int n_rows, int V, const float *temperature,
