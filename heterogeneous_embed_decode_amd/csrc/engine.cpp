@@ -490,9 +490,12 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
     LCHK(launch_gemm(eng->hl, d, (const uint16_t *)eng->w.lm_head, d, logits, c.vocab, G, c.vocab, d, EPI_F32,
                      0, 1.f, nullptr, s),
          "lm_head");
-  if (n_segs)
+  if (n_segs) {
+    bool any_l2 = false;  // an emitted embedding is scaled to unit length
+    for (size_t q = 0; q < n_segs; ++q) any_l2 |= (p.pool_segs[q * 8 + 3] & ORTHRUS_POOL_L2) && p.pool_segs[q * 8 + 5];
     LCHK(launch_pool(eng->hf, d_segs, (int)n_segs, pool->sum, pool->wsum, pool->kept, pool->buf,
-                     pool->buf_rows, emb, d, s), "pool");
+                     pool->buf_rows, emb, d, any_l2, s), "pool");
+  }
   return ORTHRUS_OK;
 }
 

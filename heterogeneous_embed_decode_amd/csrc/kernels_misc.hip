@@ -361,7 +361,7 @@ int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_ro
 }
 
 int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, float *wsum, float *kept, float *buf,
-                int buf_rows, float *emb, int d, void *stream) {
+                int buf_rows, float *emb, int d, bool any_l2, void *stream) {
   if (n_segs <= 0) return 0;
   hipLaunchKernelGGL(pool_kernel, dim3(n_segs, (d + 255) / 256), dim3(256), 0, (hipStream_t)stream, hf,
                      segs, sum, wsum, kept, buf, buf_rows, emb, d);
@@ -369,8 +369,10 @@ int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, fl
   hipLaunchKernelGGL(pool_wsum_kernel, dim3((n_segs + 63) / 64), dim3(64), 0, (hipStream_t)stream, segs,
                      n_segs, wsum);
   ORTHRUS_LAUNCH_CHECK();
-  hipLaunchKernelGGL(pool_l2_kernel, dim3(n_segs), dim3(256), 0, (hipStream_t)stream, segs, emb, d);
-  ORTHRUS_LAUNCH_CHECK();
+  if (any_l2) {  // some segment's head carries ORTHRUS_POOL_L2
+    hipLaunchKernelGGL(pool_l2_kernel, dim3(n_segs), dim3(256), 0, (hipStream_t)stream, segs, emb, d);
+    ORTHRUS_LAUNCH_CHECK();
+  }
   return 0;
 }
 

@@ -90,6 +90,6 @@ int launch_sample(const float *logits, int64_t ld, int n_rows, int V, const floa
                   const float *top_p, const uint32_t *uniforms, int32_t *tokens, void *stream);
 int launch_hash_fill(uint16_t *dst, uint64_t n, uint32_t seed, uint32_t tensor_id, uint64_t start, void *stream);
 int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, float *wsum, float *kept, float *buf,
-                int buf_rows, float *emb, int d, void *stream);
+                int buf_rows, float *emb, int d, bool any_l2, void *stream);
 
 }  // namespace orthrus
