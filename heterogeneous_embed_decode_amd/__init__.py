@@ -97,6 +97,8 @@ def _load():
     lib.orthrus_sample.restype = ctypes.c_int
     lib.orthrus_fill_hash_bf16.argtypes = [_vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64, _vp]
     lib.orthrus_fill_hash_bf16.restype = ctypes.c_int
+    lib.orthrus_set_layer_dump.argtypes = [_vp, _vp, ctypes.c_int64]
+    lib.orthrus_set_layer_dump.restype = ctypes.c_int
     lib.orthrus_profile.argtypes = [_vp, _i32]
     lib.orthrus_profile.restype = ctypes.c_int
     lib.orthrus_profile_read.argtypes = [_vp, ctypes.c_char_p, _i32]
@@ -121,7 +123,7 @@ EXPORTS = ("orthrus_pack", "orthrus_create", "orthrus_step", "orthrus_last_error
            "orthrus_destroy", "orthrus_gemm_bf16", "orthrus_profile", "orthrus_profile_read",
            "orthrus_fill_hash_bf16", "orthrus_sched_create", "orthrus_sched_submit",
            "orthrus_sched_next", "orthrus_sched_commit", "orthrus_sched_stats", "orthrus_sched_destroy",
-           "orthrus_sample")
+           "orthrus_sample", "orthrus_set_layer_dump")
 
 
 class OrthrusError(RuntimeError):
@@ -224,6 +226,11 @@ def orthrus_destroy(eng) -> None:
 
 def orthrus_gemm_bf16(A, lda, B, ldb, C, ldc, M, N, K, epilogue, b_up_row=0, stream=None) -> int:
     return LIB.orthrus_gemm_bf16(A, lda, B, ldb, C, ldc, M, N, K, epilogue, b_up_row, stream)
+
+
+def orthrus_set_layer_dump(eng, dst, cap_rows) -> int:
+    """dst: device address of fp32 [n_layers][cap_rows][d], or None to stop."""
+    return LIB.orthrus_set_layer_dump(eng, dst, cap_rows if dst else 0)
 
 
 def orthrus_profile(eng, enable: bool) -> int:

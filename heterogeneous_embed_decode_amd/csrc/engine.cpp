@@ -33,7 +33,15 @@ struct orthrus_engine {
   size_t meta_cap = 0;  // int32 words
   hipEvent_t staged{};
   bool staged_pending = false;
+  // end of the last step's work, and its stream: a step on another stream
+  // waits for it before reusing the workspace and metadata buffers
+  hipEvent_t done{};
+  hipStream_t last_stream = nullptr;
+  bool done_pending = false;
   std::string err;
+  // per-layer residual dump (opt-in): [n_layers][dump_cap][d] fp32
+  float *dump = nullptr;
+  int64_t dump_cap = 0;
   // per-kernel event timing (opt-in)
   bool profiling = false;
   struct Mark {
@@ -174,6 +182,7 @@ static void free_all(orthrus_engine *e) {
     if (p) (void)hipFree(p);
   if (e->meta_host) (void)hipHostFree(e->meta_host);
   if (e->staged) (void)hipEventDestroy(e->staged);
+  if (e->done) (void)hipEventDestroy(e->done);
 }
 
 orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weights *w, void *k_pages,
@@ -246,7 +255,8 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
   for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / hd);
   if ((r = hipMemcpy(eng->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice)) != hipSuccess)
     return bail(ORTHRUS_EHIP, "hipMemcpy", r);
-  if ((r = hipEventCreateWithFlags(&eng->staged, hipEventDisableTiming)) != hipSuccess)
+  if ((r = hipEventCreateWithFlags(&eng->staged, hipEventDisableTiming)) != hipSuccess ||
+      (r = hipEventCreateWithFlags(&eng->done, hipEventDisableTiming)) != hipSuccess)
     return bail(ORTHRUS_EHIP, "hipEventCreate", r);
   g_create_err.clear();
   *out = eng;
@@ -305,6 +315,10 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
       if (batch->items[i].kind == ORTHRUS_EMBED && batch->items[i].is_last) emb_req_ids[k++] = batch->items[i].req_id;
   }
   const int T = p.n_tokens;
+  if (eng->dump && T > eng->dump_cap) {
+    eng->err = "batch has more rows than the layer dump holds";
+    return ORTHRUS_ECAPACITY;
+  }
   if (T == 0) return ORTHRUS_OK;
 
   int n_parts = 0, n_chunk = 0;
@@ -414,6 +428,8 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   if (!eng->items.empty()) memcpy(mh + o_items, eng->items.data(), eng->items.size() * 32);
   if (!eng->work.empty()) memcpy(mh + o_work, eng->work.data(), eng->work.size() * 32);
   if (!norm_rows.empty()) memcpy(mh + o_norm, norm_rows.data(), norm_rows.size() * 4);
+  if (eng->done_pending && eng->last_stream != s)
+    HIPCHK(hipStreamWaitEvent(s, eng->done, 0), "hipStreamWaitEvent");
   HIPCHK(hipMemcpyAsync(eng->meta_dev, mh, words * 4, hipMemcpyHostToDevice, s), "metadata upload");
   HIPCHK(hipEventRecord(eng->staged, s), "hipEventRecord");
   eng->staged_pending = true;
@@ -479,6 +495,10 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
     LCHK(launch_gemm(eng->act, F, (const uint16_t *)L.w_down, F, eng->x, d, T, d, F, EPI_RESID, 0, 1.f,
                      nullptr, s),
          "gemm_down");
+    if (eng->dump)
+      HIPCHK(hipMemcpyAsync(eng->dump + (size_t)l * eng->dump_cap * d, eng->x, (size_t)T * d * 4,
+                            hipMemcpyDeviceToDevice, s),
+             "layer dump copy");
   }
   if (hidden_out)
     HIPCHK(hipMemcpyAsync(hidden_out, eng->x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s), "hidden copy");
@@ -496,6 +516,16 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
     LCHK(launch_pool(eng->hf, d_segs, (int)n_segs, pool->sum, pool->wsum, pool->kept, pool->buf,
                      pool->buf_rows, emb, d, any_l2, s), "pool");
   }
+  HIPCHK(hipEventRecord(eng->done, s), "hipEventRecord");
+  eng->last_stream = s;
+  eng->done_pending = true;
+  return ORTHRUS_OK;
+}
+
+orthrus_status orthrus_set_layer_dump(orthrus_engine *eng, float *dst, int64_t cap_rows) {
+  if (!eng || (dst && cap_rows < 1)) return ORTHRUS_EINVAL;
+  eng->dump = dst;
+  eng->dump_cap = dst ? cap_rows : 0;
   return ORTHRUS_OK;
 }
 

@@ -172,7 +172,11 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
 
 /* Run one step on `stream` (a hipStream_t; NULL = default stream).
  * Asynchronous: outputs are valid once the stream has synchronised.  The
- * batch's host arrays may be reused as soon as the call returns.
+ * batch's host arrays may be reused as soon as the call returns.  Steps of
+ * one engine run in call order: a step issued on a different stream than
+ * the previous step first waits (on the device) for the previous step's
+ * work, since both use the engine's workspace.  Calls on one engine from
+ * several host threads at once are not supported.
  *  logits      device fp32 [logits_cap_rows][vocab]: rows in item order
  *              (prefill items with is_last, then decode items)
  *  emb         device fp32 [emb_cap_rows][d]: embedding items with is_last,
@@ -201,6 +205,16 @@ const char *orthrus_last_error(const orthrus_engine *eng);
 
 /* Free the engine's workspace.  Waits for its pending work. */
 void orthrus_destroy(orthrus_engine *eng);
+
+/* Per-layer residual dump, for checking each layer of a deep model on its
+ * own (feed a layer the GPU's own input and compare its output).  While
+ * dst is set, every orthrus_step copies the fp32 residual stream after
+ * layer l (rows 0 .. n_tokens-1, [n_tokens][d]) to dst + l * cap_rows * d,
+ * on the step's stream.  dst: device fp32 [n_layers][cap_rows][d], owned
+ * by the caller, NULL to stop.  A step with more than cap_rows rows
+ * returns ECAPACITY before any device work.  EINVAL for a NULL engine or
+ * cap_rows < 1 with a non-NULL dst. */
+orthrus_status orthrus_set_layer_dump(orthrus_engine *eng, float *dst, int64_t cap_rows);
 
 /* Per-kernel timing.  While enabled, every kernel launch of orthrus_step is
  * bracketed by HIP events recorded on the step's stream (the stream the

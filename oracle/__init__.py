@@ -19,10 +19,10 @@ in their docstrings.  Every other function is pinned by ``tests/oracle``.
 """
 
 from .pack import pack_py, PackError, OK, EINVAL, ENOPAGES, ECAPACITY, ESTATE
-from .forward import (rmsnorm, rope, silu, attend_item, step, StepOut,
+from .forward import (rmsnorm, rope, silu, attend_item, layer, step, StepOut,
                       widen_weights, new_pool, new_kv)
 from .pooling import pool_item
 
 __all__ = ["pack_py", "PackError", "OK", "EINVAL", "ENOPAGES", "ECAPACITY", "ESTATE",
-           "rmsnorm", "rope", "silu", "attend_item", "step", "StepOut", "widen_weights",
+           "rmsnorm", "rope", "silu", "attend_item", "layer", "step", "StepOut", "widen_weights",
            "new_pool", "new_kv", "pool_item"]

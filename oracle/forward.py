@@ -138,60 +138,85 @@ class StepOut:
     meta: dict
 
 
-def step(cfg, W, batch, kv, pool, dtype=np.float32, limits=None):
+def layer(cfg, W, l, x, batch, meta, kv, dtype=np.float32, trace=None):
+    """Decoder layer ``l`` applied to the residual stream ``x`` [T, d] of
+    ``batch`` (packing ``meta`` from ``pack_py``); appends every row's K/V to
+    ``kv`` and returns the new residual stream.
+
+    ``trace``, when a dict, receives this layer's intermediate values (for
+    pins of single parts): ``qkv`` (the projections before RoPE, LoRA
+    included), ``o`` (attention output [T, Hq*hd]), ``x_attn`` (residual
+    after the attention block), ``h2`` (the FFN's normalised input) and
+    ``act`` (silu(gate) * up).
+    """
+    K, V = kv
+    T = batch.n_tokens
+    Hq, Hkv, hd, F = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim
+    r, s = cfg.lora_rank, dtype(cfg.lora_scale)
+    qd, kd = cfg.q_dim, cfg.kv_dim
+    ps = cfg.page_size
+    TE = meta["n_embed_rows"]
+    cu, pos = meta["cu_q"], meta["pos"]
+    p = f"layers.{l}."
+    h = rmsnorm(x, W[p + "g_attn"], dtype(cfg.rms_eps))
+    qkv = h @ W[p + "w_qkv"].T
+    if r > 0 and TE > 0:
+        A, B = W[p + "lora_a_qkv"], W[p + "lora_b_qkv"]
+        he = h[:TE]
+        qkv[:TE, :qd] += _lora(he, A[:r], B[:qd], s)
+        qkv[:TE, qd:qd + kd] += _lora(he, A[r:2 * r], B[qd:qd + kd], s)
+        qkv[:TE, qd + kd:] += _lora(he, A[2 * r:], B[qd + kd:], s)
+    q = rope(qkv[:, :qd].reshape(T, Hq, hd), pos, cfg.rope_theta)
+    k = rope(qkv[:, qd:qd + kd].reshape(T, Hkv, hd), pos, cfg.rope_theta)
+    v = qkv[:, qd + kd:].reshape(T, Hkv, hd)
+    for i, it in enumerate(batch.items):
+        pages = batch.item_pages(i)
+        for j in range(it.n_tokens):
+            pp = it.ctx_len + j
+            K[l][pages[pp // ps], :, pp % ps, :] = k[cu[i] + j]
+            V[l][pages[pp // ps], :, pp % ps, :] = v[cu[i] + j]
+    o = np.zeros((T, Hq, hd), dtype)
+    for i, it in enumerate(batch.items):
+        pages = batch.item_pages(i)
+        L = it.ctx_len + it.n_tokens
+        Kc = _gather_ctx(K[l], pages, ps, L)
+        Vc = _gather_ctx(V[l], pages, ps, L)
+        o[cu[i]:cu[i + 1]] = attend_item(q[cu[i]:cu[i + 1]], Kc, Vc, it.ctx_len)
+    o = o.reshape(T, qd)
+    delta = o @ W[p + "w_o"].T
+    if r > 0 and TE > 0:
+        delta[:TE] += _lora(o[:TE], W[p + "lora_a_o"], W[p + "lora_b_o"], s)
+    x = x + delta
+    h2 = rmsnorm(x, W[p + "g_ffn"], dtype(cfg.rms_eps))
+    gu = h2 @ W[p + "w_gate_up"].T
+    a = silu(gu[:, :F]) * gu[:, F:]
+    if trace is not None:
+        trace.update(qkv=qkv, o=o, x_attn=x, h2=h2, act=a)
+    return x + a @ W[p + "w_down"].T
+
+
+def step(cfg, W, batch, kv, pool, dtype=np.float32, limits=None, trace=None):
     """Run one forward step of ``batch``; update ``kv`` and ``pool`` in place.
 
     W: widened weights (see ``widen_weights``), kv: (K, V) lists per layer.
+    ``trace``, when a list, receives one dict per layer (see ``layer``) with
+    the layer's input residual stream under ``x_in``.
     """
     K, V = kv
     if limits is None:
         limits = Limits(n_pages=K[0].shape[0] if K else 0, max_tokens=1 << 30,
                         max_items=1 << 30, max_pool_slots=pool["sum"].shape[0])
     meta = pack_py(cfg, batch, limits)
-    T = batch.n_tokens
-    d, Hq, Hkv, hd, F = cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim
-    r, s = cfg.lora_rank, dtype(cfg.lora_scale)
-    qd, kd = cfg.q_dim, cfg.kv_dim
-    ps = cfg.page_size
-    TE = meta["n_embed_rows"]
-    cu, pos = meta["cu_q"], meta["pos"]
+    d = cfg.d_model
+    cu = meta["cu_q"]
 
     x = W["tok_emb"][batch.token_ids].astype(dtype)
     for l in range(cfg.n_layers):
-        p = f"layers.{l}."
-        h = rmsnorm(x, W[p + "g_attn"], dtype(cfg.rms_eps))
-        qkv = h @ W[p + "w_qkv"].T
-        if r > 0 and TE > 0:
-            A, B = W[p + "lora_a_qkv"], W[p + "lora_b_qkv"]
-            he = h[:TE]
-            qkv[:TE, :qd] += _lora(he, A[:r], B[:qd], s)
-            qkv[:TE, qd:qd + kd] += _lora(he, A[r:2 * r], B[qd:qd + kd], s)
-            qkv[:TE, qd + kd:] += _lora(he, A[2 * r:], B[qd + kd:], s)
-        q = rope(qkv[:, :qd].reshape(T, Hq, hd), pos, cfg.rope_theta)
-        k = rope(qkv[:, qd:qd + kd].reshape(T, Hkv, hd), pos, cfg.rope_theta)
-        v = qkv[:, qd + kd:].reshape(T, Hkv, hd)
-        for i, it in enumerate(batch.items):
-            pages = batch.item_pages(i)
-            for j in range(it.n_tokens):
-                pp = it.ctx_len + j
-                K[l][pages[pp // ps], :, pp % ps, :] = k[cu[i] + j]
-                V[l][pages[pp // ps], :, pp % ps, :] = v[cu[i] + j]
-        o = np.zeros((T, Hq, hd), dtype)
-        for i, it in enumerate(batch.items):
-            pages = batch.item_pages(i)
-            L = it.ctx_len + it.n_tokens
-            Kc = _gather_ctx(K[l], pages, ps, L)
-            Vc = _gather_ctx(V[l], pages, ps, L)
-            o[cu[i]:cu[i + 1]] = attend_item(q[cu[i]:cu[i + 1]], Kc, Vc, it.ctx_len)
-        o = o.reshape(T, qd)
-        delta = o @ W[p + "w_o"].T
-        if r > 0 and TE > 0:
-            delta[:TE] += _lora(o[:TE], W[p + "lora_a_o"], W[p + "lora_b_o"], s)
-        x = x + delta
-        h2 = rmsnorm(x, W[p + "g_ffn"], dtype(cfg.rms_eps))
-        gu = h2 @ W[p + "w_gate_up"].T
-        a = silu(gu[:, :F]) * gu[:, F:]
-        x = x + a @ W[p + "w_down"].T
+        t = None
+        if trace is not None:
+            t = {"x_in": x}
+            trace.append(t)
+        x = layer(cfg, W, l, x, batch, meta, kv, dtype, trace=t)
     hf = rmsnorm(x, W["g_final"], dtype(cfg.rms_eps))
     lr = meta["logit_rows"]
     logits = hf[lr] @ W["lm_head"].T

@@ -6,7 +6,7 @@ import numpy as np
 import oracle
 from synth import model as sm
 from synth import workloads as wl
-from tests._util import rel_l2, cosine
+from tests._util import rel_l2, row_rel_l2, cosine
 
 # Acceptance bars: rel-L2 on logits and hidden states, cosine on pooled
 # embeddings (bf16 compute against the fp32 oracle).
@@ -57,6 +57,8 @@ def run_and_compare(dims, dev, orc, batch, check_kv=True, dtype=np.float32, tag=
     assert np.array_equal(got["logit_req"], ref.logit_req), (tag, "logit req ids")
     assert np.array_equal(got["emb_req"], ref.emb_req), (tag, "embedding req ids")
     res["hidden"] = rel_l2(got["hidden"], ref.hidden)
+    rows = row_rel_l2(got["hidden"], ref.hidden)
+    res["hidden_row_max"] = float(rows.max()) if rows.size else 0.0
     if ref.logits.size:
         res["logits"] = rel_l2(got["logits"], ref.logits)
         for i in range(ref.logits.shape[0]):
@@ -64,17 +66,20 @@ def run_and_compare(dims, dev, orc, batch, check_kv=True, dtype=np.float32, tag=
     if ref.emb.size:
         res["emb_cos_min"] = min(cosine(got["emb"][i], ref.emb[i]) for i in range(ref.emb.shape[0]))
         assert res["emb_cos_min"] >= EMB_COS, (tag, res)
-    assert res["hidden"] < HIDDEN_TOL, (tag, res)
+    assert res["hidden_row_max"] < HIDDEN_TOL, (tag, res, int(rows.argmax()))
     if check_kv:
         from synth.bf16 import bf16_bits_to_f32
         slots = ref.meta["slot"]
         ps = dims.page_size
+        kv_max = 0.0
         for l in range(dims.n_layers):
             for name, tens, okv in (("K", dev.K, kv[0]), ("V", dev.V, kv[1])):
                 g = bf16_bits_to_f32(tens[l].cpu().numpy().view(np.uint16))[slots // ps, :, slots % ps, :]
                 r = okv[l][slots // ps, :, slots % ps, :]
-                e = rel_l2(g, r)
-                assert e < HIDDEN_TOL, (tag, name, l, e)
+                e = row_rel_l2(g, r)
+                kv_max = max(kv_max, float(e.max()))
+                assert e.max() < HIDDEN_TOL, (tag, name, l, float(e.max()), int(e.argmax()))
+        res["kv_row_max"] = kv_max
     print(f"[step {tag}] {res}", flush=True)
     return got, ref, res
 
@@ -86,19 +91,62 @@ def _hash_f32(seed, tid, start, n):
 
 
 def depth_tolerance(n_layers):
-    """rel-L2 bound for hidden states and logits after n_layers bf16 layers:
-    the task's 2e-2 up to 2 layers; beyond, the bf16 rounding of every GEMM
-    input accumulates at about 0.88 % per layer growing as sqrt(layers)
-    (measured by emulating the GPU's rounding points in fp32 numpy on one
-    Mistral-shaped layer), so 1.1e-2 * sqrt(layers)."""
+    """End-to-end rel-L2 bound for hidden states and logits after n_layers
+    bf16 layers against the fp32 oracle: the task's 2e-2 up to 2 layers;
+    beyond, the bf16 rounding of every GEMM operand adds an independent
+    error of about 0.9 % of the row per layer, so the end-to-end error
+    grows as sqrt(layers) (reproduced on the CPU by
+    tests/oracle/test_bf16_depth.py), bound 1.1e-2 * sqrt(layers).  Every
+    layer on its own is held to 2e-2 per row at full depth by the
+    teacher-forced check of run_workload_sampled."""
     return max(HIDDEN_TOL, 1.1e-2 * np.sqrt(n_layers))
 
 
-def run_workload_sampled(w, n_emb, n_dec, tag="", seed=11, want_steps=None):
+def _teacher_forced_layers(cfg, W, dev, dump, sub, g_rows, inv_pages, tag):
+    """Each layer of the GPU step against the oracle's layer fed the GPU's
+    own input: layer l gets the GPU residual after layer l-1 (the token
+    embedding for l = 0) and the GPU's KV pages of layer l; its output rows
+    and the K/V it appends are compared per row at 2e-2."""
+    import torch
+    from synth.bf16 import bf16_bits_to_f32
+    from oracle.pack import Limits
+    L, ps = cfg.n_layers, cfg.page_size
+    meta = oracle.pack_py(cfg, sub, Limits(n_pages=len(inv_pages), max_tokens=1 << 30, max_items=1 << 30,
+                                          max_pool_slots=1 << 20))
+    slots = meta["slot"]
+    idx = torch.as_tensor(np.asarray(inv_pages, np.int64), device=dev.device)
+    rows_t = torch.as_tensor(np.asarray(g_rows, np.int64), device=dev.device)
+    worst = {"x": 0.0, "k": 0.0, "v": 0.0}
+    x_in = W["tok_emb"][sub.token_ids].astype(np.float32)
+    for l in range(L):
+        Kl = bf16_bits_to_f32(dev.K[l].index_select(0, idx).cpu().numpy().view(np.uint16))
+        Vl = bf16_bits_to_f32(dev.V[l].index_select(0, idx).cpu().numpy().view(np.uint16))
+        gk = Kl[slots // ps, :, slots % ps, :].copy()
+        gv = Vl[slots // ps, :, slots % ps, :].copy()
+        kv = ({l: Kl}, {l: Vl})
+        x_ref = oracle.layer(cfg, W, l, x_in, sub, meta, kv, np.float32)
+        x_gpu = dump[l].index_select(0, rows_t).cpu().numpy()
+        ex = row_rel_l2(x_gpu, x_ref)
+        ek = row_rel_l2(gk, Kl[slots // ps, :, slots % ps, :])
+        ev = row_rel_l2(gv, Vl[slots // ps, :, slots % ps, :])
+        worst["x"] = max(worst["x"], float(ex.max()))
+        worst["k"] = max(worst["k"], float(ek.max()))
+        worst["v"] = max(worst["v"], float(ev.max()))
+        assert ex.max() < HIDDEN_TOL, (tag, "layer", l, "residual row", int(ex.argmax()), float(ex.max()))
+        assert ek.max() < HIDDEN_TOL, (tag, "layer", l, "K row", int(ek.argmax()), float(ek.max()))
+        assert ev.max() < HIDDEN_TOL, (tag, "layer", l, "V row", int(ev.argmax()), float(ev.max()))
+        x_in = x_gpu
+    print(f"[{tag}] teacher-forced per-layer row maxima over {L} layers: {worst}", flush=True)
+    return worst
+
+
+def run_workload_sampled(w, n_emb, n_dec, tag="", seed=11, want_steps=None, teacher_steps=()):
     """Run every step of workload `w` on the GPU over hash-filled prior KV and
     pooling state, and check a seeded sample of requests (n_emb embedding
     requests, n_dec decode requests, every prefill item) against the oracle
-    run on those requests alone.  Returns the list of per-step error dicts."""
+    run on those requests alone, row by row.  In the steps listed in
+    teacher_steps every layer is also checked on its own (see
+    _teacher_forced_layers).  Returns the list of per-step error dicts."""
     import torch
     import heterogeneous_embed_decode_amd as hed
     from heterogeneous_embed_decode_amd.device_model import DeviceModel
@@ -121,6 +169,9 @@ def run_workload_sampled(w, n_emb, n_dec, tag="", seed=11, want_steps=None):
     for s_, v in w.prior_wsum.items():
         ws[s_] = v
     dev.pool_wsum[:w.n_slots].copy_(torch.from_numpy(ws))
+    dump = None
+    if teacher_steps:
+        dump = torch.empty((L, max_t, d), dtype=torch.float32, device=dev.device)
     torch.cuda.synchronize()
 
     # the sample: requests of the first batch, seeded choice
@@ -136,6 +187,7 @@ def run_workload_sampled(w, n_emb, n_dec, tag="", seed=11, want_steps=None):
     W = oracle.widen_weights(bits, np.float32)
     del bits
     page_map = {}
+    inv_pages = []
     blk = cfg.n_kv_heads * cfg.page_size * cfg.head_dim
     Ks = [[] for _ in range(L)]
     Vs = [[] for _ in range(L)]
@@ -149,6 +201,8 @@ def run_workload_sampled(w, n_emb, n_dec, tag="", seed=11, want_steps=None):
     for si, b in enumerate(w.batches):
         if want_steps is not None and si not in want_steps:
             continue
+        teach = si in teacher_steps
+        hed.orthrus_set_layer_dump(dev.eng, dump.data_ptr() if teach else None, max_t)
         got = dev.step_checked(b, want_hidden=True)
         cu = np.concatenate([[0], np.cumsum([it.n_tokens for it in b.items])])
         # sub-batch of the sampled requests, pages remapped
@@ -163,6 +217,7 @@ def run_workload_sampled(w, n_emb, n_dec, tag="", seed=11, want_steps=None):
                     p = int(p)
                     if p not in page_map:
                         page_map[p] = len(page_map)
+                        inv_pages.append(p)
                         for l in range(L):
                             start = (l * w.n_pages + p) * blk
                             Ks[l].append(_hash_f32(KV_SEED, 0, start, blk).reshape(cfg.n_kv_heads, cfg.page_size, cfg.head_dim))
@@ -183,13 +238,20 @@ def run_workload_sampled(w, n_emb, n_dec, tag="", seed=11, want_steps=None):
         if not items:
             continue
         sub = Batch(items, np.asarray(toks, np.int32), np.asarray(pages, np.int32))
+        n_kinds = {k: sum(1 for it in items if it.kind == k) for k in (EMBED, PREFILL, DECODE)}
+        print(f"[{tag}] step {si}: sampled items embed/prefill/decode = "
+              f"{n_kinds[EMBED]}/{n_kinds[PREFILL]}/{n_kinds[DECODE]}, {len(g_rows)} rows", flush=True)
+        res = {"step": si, "items": len(items)}
+        if teach:
+            res["teacher"] = _teacher_forced_layers(cfg, W, dev, dump, sub, g_rows, inv_pages, f"{tag} step {si}")
         kv = ([np.stack(Ks[l]) for l in range(L)], [np.stack(Vs[l]) for l in range(L)])
         ref = oracle.step(cfg, W, sub, kv, pool, np.float32)
         for l in range(L):  # keep what the oracle appended
             Ks[l] = list(kv[0][l])
             Vs[l] = list(kv[1][l])
-        res = {"step": si, "items": len(items)}
+        rows = row_rel_l2(got["hidden"][g_rows], ref.hidden)
         res["hidden"] = rel_l2(got["hidden"][g_rows], ref.hidden)
+        res["hidden_row_max"] = float(rows.max())
         if g_logit:
             errs = [rel_l2(got["logits"][g], ref.logits[k]) for k, g in enumerate(g_logit)]
             res["logits_max"] = max(errs)
@@ -197,7 +259,7 @@ def run_workload_sampled(w, n_emb, n_dec, tag="", seed=11, want_steps=None):
             coss = [cosine(got["emb"][g], ref.emb[k]) for k, g in enumerate(g_emb)]
             res["emb_cos_min"] = min(coss)
         print(f"[{tag}] tol={tol:.4f} cos_bar={cos_bar:.5f} {res}", flush=True)
-        assert res["hidden"] < tol, (tag, res)
+        assert res["hidden_row_max"] < tol, (tag, res, int(rows.argmax()))
         assert res.get("logits_max", 0.0) < tol, (tag, res)
         assert res.get("emb_cos_min", 1.0) >= cos_bar, (tag, res)
         for slot, kind in pool_checks:
@@ -212,5 +274,6 @@ def run_workload_sampled(w, n_emb, n_dec, tag="", seed=11, want_steps=None):
             assert c >= cos_bar, (tag, res)
         print(f"[{tag}] {res}", flush=True)
         results.append(res)
+    hed.orthrus_set_layer_dump(dev.eng, None, 0)
     dev.close()
     return results

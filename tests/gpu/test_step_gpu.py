@@ -79,6 +79,30 @@ def test_tiny_lora_mixed_heads():
     dev.close()
 
 
+@pytest.mark.parametrize("scale", [0.5, 2.0])
+def test_tiny_lora_scale(scale):
+    """Adapter scale other than 1 (folded into the shrink epilogue on the
+    GPU): the tiny model's q/k/v sections (64/32/32 columns) share one
+    output tile, so the section offsets of the expand K-steps are exercised
+    inside a tile; and a d=128 model with rank 16 on a random batch."""
+    cfg = sm.TINY.with_(lora_rank=8, lora_scale=scale)
+    bits = sm.make_weights(cfg, seed=3, gain_std=0.1)
+    _, batches, n_pages = wl.tiny_workload(cfg=cfg, pool_kind=wl.POOL_MEAN, chunk=7)
+    dev, orc = make_pair(cfg, n_pages, bits)
+    for s, b in enumerate(batches):
+        run_and_compare(cfg, dev, orc, b, tag=f"tiny-lora scale={scale} step={s}")
+    dev.close()
+    base = sm.ModelConfig(n_layers=1, d_model=128, n_q_heads=8, n_kv_heads=2, head_dim=16, ffn_dim=96,
+                          vocab=300, lora_rank=16, page_size=8, rope_theta=1e4, lora_scale=scale)
+    b, n_pages = wl.random_batch(base, 78, max_items=12, max_len=120, max_ctx=300)
+    bits = sm.make_weights(base, seed=8, gain_std=0.1)
+    kv = wl.synthetic_kv(base, n_pages, seed=3)
+    dev, orc = make_pair(base, n_pages, bits, kv_bits=kv)
+    seed_pool(dev, orc, 9)
+    run_and_compare(base, dev, orc, b, tag=f"random lora scale={scale}")
+    dev.close()
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_random_ragged_batches(seed):
     base = [sm.TINY.with_(lora_rank=8),

@@ -1,10 +1,11 @@
 """Parity on the large mixed workloads at their full batch sizes (8192-token
 budgets, 256-819 decode rows, LoRA ranks 16/64, mean / weighted-mean / CLS
 pooling with synthetic prior state, Llama-3.1 vocabulary), on a seeded
-sample of requests recomputed alone by the oracle.  Depths are reduced
-(the layers repeat the same kernels) except for the 1:9 workload, which runs
-all 32 layers to check that bf16 error stays within bounds over the full
-depth."""
+sample of at least 4 embedding requests, 8 decode requests and every
+prefill item, recomputed alone by the oracle and compared row by row.
+At 2 layers the end-to-end bar is the task's 2e-2; at the full 32 layers
+every layer is also checked on its own (teacher-forced, fed the GPU's input)
+at 2e-2 per row, and the end-to-end state against the bf16 depth bound."""
 
 import pytest
 
@@ -16,30 +17,31 @@ pytestmark = pytest.mark.gpu
 
 def test_nine_to_one_ten_steps_carried_state():
     w = wl.nine_to_one_workload(n_layers=2)
-    res = run_workload_sampled(w, n_emb=3, n_dec=8, tag="9:1 x10")
+    res = run_workload_sampled(w, n_emb=4, n_dec=8, tag="9:1 x10")
     assert len(res) == 10
 
 
 def test_five_to_five_rank64_weighted_mean():
     w = wl.five_to_five_workload(n_layers=2)
-    run_workload_sampled(w, n_emb=2, n_dec=8, tag="5:5")
+    run_workload_sampled(w, n_emb=4, n_dec=8, tag="5:5")
 
 
 def test_one_to_nine_llama_cls():
     w = wl.one_to_nine_workload(n_layers=2)
-    run_workload_sampled(w, n_emb=3, n_dec=8, tag="1:9")
+    run_workload_sampled(w, n_emb=4, n_dec=8, tag="1:9")
 
 
 def test_one_to_nine_full_depth():
     w = wl.one_to_nine_workload(n_layers=32)
-    run_workload_sampled(w, n_emb=1, n_dec=4, tag="1:9 x32 layers")
+    run_workload_sampled(w, n_emb=4, n_dec=8, tag="1:9 x32 layers", teacher_steps=(0,))
 
 
 def test_five_to_five_full_depth():
     w = wl.five_to_five_workload(n_layers=32)
-    run_workload_sampled(w, n_emb=1, n_dec=4, tag="5:5 x32 layers")
+    run_workload_sampled(w, n_emb=4, n_dec=8, tag="5:5 x32 layers", teacher_steps=(0,))
 
 
-def test_nine_to_one_full_depth_three_steps():
-    w = wl.nine_to_one_workload(n_layers=32, steps=3)
-    run_workload_sampled(w, n_emb=1, n_dec=4, tag="9:1 x32 layers")
+def test_nine_to_one_full_depth_ten_steps():
+    w = wl.nine_to_one_workload(n_layers=32, steps=10)
+    res = run_workload_sampled(w, n_emb=4, n_dec=8, tag="9:1 x32 layers", teacher_steps=(0, 9))
+    assert len(res) == 10
