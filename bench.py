@@ -1,19 +1,25 @@
 """Benchmark: mixed-batch tokens/s of one heterogeneous-batch step on MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--workload W]
 
-Workload: one Mistral-7B-shaped decoder layer in bf16 (d 4096, 32 q / 8 kv
-heads of 128, SwiGLU 14336, RoPE theta 1e6, vocab 32768, N(0, 0.02)
-weights, LoRA rank 16 on q/k/v/o for embedding rows only) over a batch of
-8 embedding chunks x 512 tokens (last-token pooling) and 64 decode rows with
-KV contexts uniform in [500, 3500], KV pages of 16 tokens: 4160 rows per
-step, all inputs seeded and synthetic, already resident in HBM.
+Default workload (mix91): the full 32-layer Mistral-7B-shaped decoder in
+bf16 (d 4096, 32 q / 8 kv heads of 128, SwiGLU 14336, RoPE theta 1e6, vocab
+32768, N(0, 0.02) weights, LoRA rank 16 on q/k/v/o for embedding rows only)
+at a 9:1 embedding:generation token mix with a budget of 8192 rows per
+step: 819 decode rows with KV contexts uniform in [500, 3500] reserved
+first, then embedding requests of U[256, 4096] tokens in chunks of 256
+(mean pooling) admitted first come first served; ten consecutive distinct
+steps with KV and pooling state carried.  Inputs are seeded and synthetic
+and already resident in HBM.  Other workloads: one_layer (one such layer,
+8 x 512-token embedding chunks + 64 decode rows), mix55, mix19.
 
-A step is one orthrus_step call (embed gather, the layer, final norm, LM
-head on the 64 logit rows, pooling).  The timed region is K steps bracketed
-by device synchronisation; a second pass of K steps with per-kernel HIP
-events gives each kernel's average duration for the roofline figure.  The
-CPU baseline times the oracle on the same step on the host cores.
+A step is one orthrus_step call (embed gather, every layer, final norm, LM
+head on the logit rows, pooling); the timed region is K steps cycling
+through the distinct steps, bracketed by device synchronisation, and
+`value` is the rows of those steps over the wall time.  Further untimed
+passes give per-step times (HIP events around each step) and per-kernel
+averages (HIP events around each launch, on the step's stream) for the
+roofline figures.  The CPU baseline times the oracle on the host cores.
 """
 
 import argparse
@@ -67,6 +73,52 @@ def kernel_work(cfg, batch, meta):
         "lora_shrink_o": (2.0 * TE * r * qd, 2.0 * (TE * qd + r * qd)),
         "pool": (0.0, pool_bytes(cfg, batch)),
     }
+
+
+def step_roofline_ms(cfg, batch, meta):
+    """Ideal time of one step: every kernel at the larger of its algorithmic
+    flops over the bf16 MFMA peak and its algorithmic HBM bytes over the HBM
+    peak, summed over the step's launches (per-layer kernels times the
+    depth).  Terms: the four projections with their adapter shrinks, chunk
+    and decode attention, the two norms and the RoPE/KV append per layer,
+    and the LM head, final norm and pooling once."""
+    w = kernel_work(cfg, batch, meta)
+    L, T, d = cfg.n_layers, batch.n_tokens, cfg.d_model
+    P, BW = PEAK_BF16_TFLOPS * 1e12, PEAK_HBM_GBS * 1e9
+
+    def t(fl, by):
+        return max(fl / P, by / BW)
+
+    per_layer = ["gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attn_chunk", "attn_decode"]
+    if meta["n_embed_rows"] and cfg.lora_rank:
+        per_layer += ["lora_shrink_qkv", "lora_shrink_o"]
+    terms = {k: L * t(*w[k]) for k in per_layer}
+    terms["rmsnorm"] = L * 2 * t(0.0, T * d * (4.0 + 2.0))
+    terms["rope_kv"] = L * t(0.0, 2.0 * T * (cfg.q_dim + cfg.kv_dim) * 2 + 2.0 * T * 2 * cfg.kv_dim)
+    terms["final_norm"] = t(0.0, T * d * 4.0 + (meta["n_embed_rows"] + meta["n_logits"]) * d * 4.0)
+    terms["lm_head"] = t(*w["lm_head"])
+    terms["pool"] = t(*w["pool"])
+    return 1e3 * sum(terms.values()), {k: round(1e3 * v, 4) for k, v in terms.items()}
+
+
+def host_description():
+    """CPU model, logical CPUs and the BLAS numpy calls into."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas": blas}
 
 
 def pool_bytes(cfg, batch):
@@ -161,6 +213,7 @@ def cpu_baseline_one_layer(cfg, batch, n_pages, bits, n_slots, prior_wsum):
     est = dt1 * cfg.n_layers
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": batch.n_tokens / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "extrapolated": True, "host": host_description(),
             "sample": f"one full-batch layer of the first step ({batch.n_tokens} rows) through the numpy fp32 "
                       f"oracle, {dt1:.2f} s, extrapolated to {cfg.n_layers} layers (extrapolated from 1 measured "
                       f"layer)"}
@@ -178,6 +231,7 @@ def cpu_baseline(cfg, batch, n_pages, bits, kv_bits):
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": batch.n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "extrapolated": False, "host": host_description(),
             "sample": f"one full step of the same workload ({batch.n_tokens} rows) through the numpy fp32 "
                       f"oracle, {dt:.2f} s"}
 
@@ -233,9 +287,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="one_layer", choices=["one_layer", "mix91", "mix55", "mix19"],
-                    help="one_layer (default line): one Mistral-7B-shaped layer, 4160 rows; mix91/mix55/mix19: "
-                         "the 32-layer 9:1 (ten distinct steps), 5:5 (rank 64) and Llama-3.1-8B 1:9 workloads")
+    ap.add_argument("--workload", default="mix91", choices=["one_layer", "mix91", "mix55", "mix19"],
+                    help="mix91 (default): the 32-layer 9:1 workload, ten distinct steps; mix55 (rank 64) and "
+                         "mix19 (Llama-3.1-8B shape, 1:9); one_layer: one Mistral-7B-shaped layer, 4160 rows")
     ap.add_argument("--layers", type=int, default=32, help="depth of the mixed workloads")
     ap.add_argument("--pool-kind", default="last", choices=["last", "mean", "wmean", "cls", "buffer", "last+l2",
                                                               "mean+l2", "buffer+l2"],
@@ -350,6 +404,33 @@ def main():
     print(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, {ev_ms / args.steps:.3f} ms/step events",
           file=sys.stderr, flush=True)
 
+    # per distinct step: HIP events around each step on its stream
+    per_step = []
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in batches]
+    for j, b in enumerate(batches):
+        ev[j][0].record(stream)
+        s_, _, _ = dev.step(b, stream=sptr, args=bargs[j])
+        assert s_ == hed.OK
+        ev[j][1].record(stream)
+    torch.cuda.synchronize()
+    for j, b in enumerate(batches):
+        ms = ev[j][0].elapsed_time(ev[j][1])
+        roof_ms, _ = step_roofline_ms(cfg, b, metas[j])
+        per_step.append({"step": j, "rows": b.n_tokens, "embed_rows": int(metas[j]["n_embed_rows"]),
+                         "decode_rows": int(metas[j]["n_decode_rows"]), "ms": round(ms, 3),
+                         "tokens_per_s": round(b.n_tokens / (ms * 1e-3), 1), "roofline_ms": round(roof_ms, 3),
+                         "roofline_frac": round(roof_ms / ms, 4)})
+    t_roof = sum(r["roofline_ms"] for r in per_step)
+    t_meas = sum(r["ms"] for r in per_step)
+    _, terms0 = step_roofline_ms(cfg, batches[0], metas[0])
+    step_roof = {"definition": "sum over the step's launches of max(algorithmic flops / 2.5 PFLOP/s, algorithmic "
+                               "HBM bytes / 8 TB/s), over the measured step time (HIP events), summed over the "
+                               "distinct steps",
+                 "t_roof_ms": round(t_roof, 3), "t_measured_ms": round(t_meas, 3),
+                 "frac": round(t_roof / t_meas, 4), "terms_step0_ms": terms0}
+    print(f"per step: " + ", ".join(f"{r['ms']:.1f}" for r in per_step) + f" ms; step roofline fraction "
+          f"{t_roof / t_meas:.3f}", file=sys.stderr, flush=True)
+
     # per-kernel durations over an identical pass
     hed.orthrus_profile(dev.eng, True)
     run(args.steps)
@@ -415,6 +496,8 @@ def main():
                    "decode_rows": meta["n_decode_rows"], "layers": cfg.n_layers, "d_model": cfg.d_model,
                    "ffn_dim": cfg.ffn_dim, "vocab": cfg.vocab, "lora_rank": cfg.lora_rank},
         "roofline": roof,
+        "step_roofline": step_roof,
+        "per_step": per_step,
         "cpu_baseline": cpu,
         "sampler": sampler,
         "kernels": kernels,
