@@ -87,6 +87,8 @@ def _load():
     lib.orthrus_step.argtypes = [_vp, ctypes.POINTER(orthrus_batch), ctypes.POINTER(orthrus_pool_state),
                                  _vp, _i32, _vp, _i32, _i32p, _i32p, _i32p, _i32p, _vp, _vp]
     lib.orthrus_step.restype = ctypes.c_int
+    lib.orthrus_step_noalloc.argtypes = lib.orthrus_step.argtypes
+    lib.orthrus_step_noalloc.restype = ctypes.c_int
     lib.orthrus_last_error.argtypes = [_vp]
     lib.orthrus_last_error.restype = ctypes.c_char_p
     lib.orthrus_destroy.argtypes = [_vp]
@@ -123,7 +125,7 @@ EXPORTS = ("orthrus_pack", "orthrus_create", "orthrus_step", "orthrus_last_error
            "orthrus_destroy", "orthrus_gemm_bf16", "orthrus_profile", "orthrus_profile_read",
            "orthrus_fill_hash_bf16", "orthrus_sched_create", "orthrus_sched_submit",
            "orthrus_sched_next", "orthrus_sched_commit", "orthrus_sched_stats", "orthrus_sched_destroy",
-           "orthrus_sample", "orthrus_set_layer_dump")
+           "orthrus_sample", "orthrus_set_layer_dump", "orthrus_step_noalloc")
 
 
 class OrthrusError(RuntimeError):
@@ -196,11 +198,12 @@ def orthrus_create(cfg: orthrus_model_cfg, tok_emb, lm_head, g_final, layers, k_
 
 def orthrus_step(eng, batch: BatchArgs, pool_sum, pool_wsum, pool_kept, logits, logits_cap_rows,
                  emb, emb_cap_rows, hidden_out=None, stream=None, logit_req_ids=None, emb_req_ids=None,
-                 pool_buf=None, buf_rows=0):
+                 pool_buf=None, buf_rows=0, noalloc=False):
     """Returns (status, n_logits, n_emb).  logit_req_ids / emb_req_ids:
     optional int32 numpy arrays of at least logits_cap_rows / emb_cap_rows
     entries that receive the req_id of each output row.  pool_buf /
-    buf_rows: the BUFFER pooling kind's hidden-state buffer."""
+    buf_rows: the BUFFER pooling kind's hidden-state buffer.  noalloc:
+    call orthrus_step_noalloc instead (same arguments)."""
     ps = orthrus_pool_state(pool_sum, pool_wsum, pool_kept, pool_buf, buf_rows)
     nl, ne = _i32(0), _i32(0)
 
@@ -210,9 +213,10 @@ def orthrus_step(eng, batch: BatchArgs, pool_sum, pool_wsum, pool_kept, logits, 
         assert a.dtype == np.int32 and a.flags.c_contiguous and a.size >= cap
         return a.ctypes.data_as(_i32p)
 
-    st = LIB.orthrus_step(eng, ctypes.byref(batch.struct), ctypes.byref(ps), logits, logits_cap_rows,
-                          emb, emb_cap_rows, ctypes.byref(nl), ctypes.byref(ne),
-                          ids(logit_req_ids, logits_cap_rows), ids(emb_req_ids, emb_cap_rows), hidden_out, stream)
+    fn = LIB.orthrus_step_noalloc if noalloc else LIB.orthrus_step
+    st = fn(eng, ctypes.byref(batch.struct), ctypes.byref(ps), logits, logits_cap_rows,
+            emb, emb_cap_rows, ctypes.byref(nl), ctypes.byref(ne),
+            ids(logit_req_ids, logits_cap_rows), ids(emb_req_ids, emb_cap_rows), hidden_out, stream)
     return st, nl.value, ne.value
 
 

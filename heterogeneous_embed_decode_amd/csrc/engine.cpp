@@ -233,6 +233,9 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
   };
   hipError_t r = hipGetDevice(&eng->device);
   if (r != hipSuccess) return bail(ORTHRUS_EHIP, "hipGetDevice", r);
+  // the allocation-free step's static scratch: its address on this device
+  if ((r = (hipError_t)noalloc_scratch_init(eng->device)) != hipSuccess)
+    return bail(ORTHRUS_EHIP, "hipGetSymbolAddress(scratch)", r);
   const size_t T = c.max_tokens, d = c.d_model;
   const size_t qkvd = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * hd, qd = (size_t)c.n_q_heads * hd;
   struct {
@@ -255,6 +258,13 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
   for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / hd);
   if ((r = hipMemcpy(eng->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice)) != hipSuccess)
     return bail(ORTHRUS_EHIP, "hipMemcpy", r);
+  // metadata staging, pinned host and device, sized for the allocation-free
+  // step's largest metadata block; orthrus_step grows both when a batch needs more
+  eng->meta_cap = NOALLOC_META_BYTES / 4;
+  if ((r = hipMalloc(&eng->meta_dev, eng->meta_cap * 4)) != hipSuccess)
+    return bail(ORTHRUS_ENOMEM, "hipMalloc", r);
+  if ((r = hipHostMalloc(&eng->meta_host, eng->meta_cap * 4, hipHostMallocDefault)) != hipSuccess)
+    return bail(ORTHRUS_ENOMEM, "hipHostMalloc", r);
   if ((r = hipEventCreateWithFlags(&eng->staged, hipEventDisableTiming)) != hipSuccess ||
       (r = hipEventCreateWithFlags(&eng->done, hipEventDisableTiming)) != hipSuccess)
     return bail(ORTHRUS_EHIP, "hipEventCreate", r);
@@ -271,10 +281,10 @@ void orthrus_destroy(orthrus_engine *eng) {
   delete eng;
 }
 
-orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, const orthrus_pool_state *pool,
-                            float *logits, int32_t logits_cap_rows, float *emb, int32_t emb_cap_rows,
-                            int32_t *n_logits, int32_t *n_emb, int32_t *logit_req_ids, int32_t *emb_req_ids,
-                            float *hidden_out, void *stream) {
+static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch, const orthrus_pool_state *pool,
+                                float *logits, int32_t logits_cap_rows, float *emb, int32_t emb_cap_rows,
+                                int32_t *n_logits, int32_t *n_emb, int32_t *logit_req_ids, int32_t *emb_req_ids,
+                                float *hidden_out, void *stream, bool noalloc) {
   if (!eng) return ORTHRUS_EINVAL;
   eng->err.clear();
   if (!batch || !pool) {
@@ -381,11 +391,38 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   const size_t o_work = off; off = align4(off + eng->work.size() * 8);
   const size_t o_norm = off; off = align4(off + norm_rows.size());
   const size_t words = std::max<size_t>(off, 4);
+  const int Gq = c.n_q_heads / c.n_kv_heads;
+  int32_t *meta_dev = eng->meta_dev;
+  float *part_ml = eng->part_ml, *part_o = eng->part_o;
+  if (noalloc) {
+    // metadata and decode partials in the static scratch: refuse what does
+    // not fit before any device work
+    char *base = (char *)noalloc_scratch(eng->device);
+    const size_t ml_bytes = ((size_t)n_parts * Gq * 2 * 4 + 255) & ~(size_t)255;
+    const size_t o_bytes = (size_t)n_parts * Gq * c.head_dim * 4;
+    if (!base) {
+      eng->err = "static scratch not resolved on this device";
+      return ORTHRUS_EHIP;
+    }
+    if (words * 4 > NOALLOC_META_BYTES || words > eng->meta_cap) {
+      eng->err = "step metadata exceeds the allocation-free limit (" + std::to_string(NOALLOC_META_BYTES / 4) +
+                 " int32 words)";
+      return ORTHRUS_ECAPACITY;
+    }
+    if (ml_bytes + o_bytes > NOALLOC_SCRATCH_BYTES - NOALLOC_META_BYTES) {
+      eng->err = "decode partial results exceed the allocation-free scratch (" +
+                 std::to_string((NOALLOC_SCRATCH_BYTES - NOALLOC_META_BYTES) >> 20) + " MiB)";
+      return ORTHRUS_ECAPACITY;
+    }
+    meta_dev = (int32_t *)base;
+    part_ml = (float *)(base + NOALLOC_META_BYTES);
+    part_o = (float *)(base + NOALLOC_META_BYTES + ml_bytes);
+  }
   if (eng->staged_pending) {
     HIPCHK(hipEventSynchronize(eng->staged), "hipEventSynchronize");
     eng->staged_pending = false;
   }
-  if (words > eng->meta_cap) {
+  if (!noalloc && words > eng->meta_cap) {
     const size_t cap = words * 2;
     if (eng->meta_dev) {
       HIPCHK(hipDeviceSynchronize(), "hipDeviceSynchronize");
@@ -401,21 +438,23 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
       return ORTHRUS_ENOMEM;
     }
     eng->meta_cap = cap;
+    meta_dev = eng->meta_dev;
   }
-  if ((size_t)n_parts > eng->part_cap) {
+  if (!noalloc && (size_t)n_parts > eng->part_cap) {
     const size_t cap = (size_t)n_parts * 2;
     HIPCHK(hipDeviceSynchronize(), "hipDeviceSynchronize");
     if (eng->part_ml) (void)hipFree(eng->part_ml);
     if (eng->part_o) (void)hipFree(eng->part_o);
     eng->part_ml = eng->part_o = nullptr;
     eng->part_cap = 0;
-    const int Gq = c.n_q_heads / c.n_kv_heads;
     if (hipMalloc(&eng->part_ml, cap * Gq * 2 * 4) != hipSuccess ||
         hipMalloc(&eng->part_o, cap * Gq * (size_t)c.head_dim * 4) != hipSuccess) {
       eng->err = "partial buffer allocation failed";
       return ORTHRUS_ENOMEM;
     }
     eng->part_cap = cap;
+    part_ml = eng->part_ml;
+    part_o = eng->part_o;
   }
   int32_t *mh = eng->meta_host;
   memcpy(mh + o_tok, batch->token_ids, (size_t)T * 4);
@@ -430,16 +469,16 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   if (!norm_rows.empty()) memcpy(mh + o_norm, norm_rows.data(), norm_rows.size() * 4);
   if (eng->done_pending && eng->last_stream != s)
     HIPCHK(hipStreamWaitEvent(s, eng->done, 0), "hipStreamWaitEvent");
-  HIPCHK(hipMemcpyAsync(eng->meta_dev, mh, words * 4, hipMemcpyHostToDevice, s), "metadata upload");
+  HIPCHK(hipMemcpyAsync(meta_dev, mh, words * 4, hipMemcpyHostToDevice, s), "metadata upload");
   HIPCHK(hipEventRecord(eng->staged, s), "hipEventRecord");
   eng->staged_pending = true;
 
-  const int32_t *d_tok = eng->meta_dev + o_tok, *d_pos = eng->meta_dev + o_pos;
-  const int32_t *d_slot = eng->meta_dev + o_slot, *d_pages = eng->meta_dev + o_pages;
-  const int32_t *d_logit = eng->meta_dev + o_logit, *d_segs = eng->meta_dev + o_segs;
-  const int32_t *d_dec = eng->meta_dev + o_dec;
-  const DevItem *d_items = (const DevItem *)(eng->meta_dev + o_items);
-  const AttnWork *d_work = (const AttnWork *)(eng->meta_dev + o_work);
+  const int32_t *d_tok = meta_dev + o_tok, *d_pos = meta_dev + o_pos;
+  const int32_t *d_slot = meta_dev + o_slot, *d_pages = meta_dev + o_pages;
+  const int32_t *d_logit = meta_dev + o_logit, *d_segs = meta_dev + o_segs;
+  const int32_t *d_dec = meta_dev + o_dec;
+  const DevItem *d_items = (const DevItem *)(meta_dev + o_items);
+  const AttnWork *d_work = (const AttnWork *)(meta_dev + o_work);
 
   const int d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, F = c.ffn_dim;
   const int qd = Hq * hd, kvd = Hkv * hd, qkvd = qd + 2 * kvd, r = c.lora_rank;
@@ -474,10 +513,10 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
            "attn_chunk");
     if (n_dec_work > 0)
       LCHK(launch_attn_decode(eng->qkv, qkvd, kc, vc, d_pages, d_items, d_work + n_chunk, n_dec_work,
-                              eng->part_ml, eng->part_o, eng->o, qd, Hq, Hkv, hd, c.page_size, s),
+                              part_ml, part_o, eng->o, qd, Hq, Hkv, hd, c.page_size, s),
            "attn_decode");
     if (multi_split)
-      LCHK(launch_attn_combine(d_items, d_dec, (int)dec_items.size(), eng->part_ml, eng->part_o, eng->o, qd,
+      LCHK(launch_attn_combine(d_items, d_dec, (int)dec_items.size(), part_ml, part_o, eng->o, qd,
                                Hq, Hkv, hd, s),
            "attn_combine");
     if (lora) {
@@ -503,7 +542,7 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   if (hidden_out)
     HIPCHK(hipMemcpyAsync(hidden_out, eng->x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s), "hidden copy");
   LCHK(launch_final_norm(eng->x, (const uint16_t *)eng->w.g_final, d_logit,
-                         norm_subset ? eng->meta_dev + o_norm : nullptr,
+                         norm_subset ? meta_dev + o_norm : nullptr,
                          norm_subset ? (int)norm_rows.size() : TE, G, eng->hf, eng->hl, d, c.rms_eps, s),
        "final_norm");
   if (G > 0)
@@ -520,6 +559,22 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, con
   eng->last_stream = s;
   eng->done_pending = true;
   return ORTHRUS_OK;
+}
+
+orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch, const orthrus_pool_state *pool,
+                            float *logits, int32_t logits_cap_rows, float *emb, int32_t emb_cap_rows,
+                            int32_t *n_logits, int32_t *n_emb, int32_t *logit_req_ids, int32_t *emb_req_ids,
+                            float *hidden_out, void *stream) {
+  return step_impl(eng, batch, pool, logits, logits_cap_rows, emb, emb_cap_rows, n_logits, n_emb, logit_req_ids,
+                   emb_req_ids, hidden_out, stream, false);
+}
+
+orthrus_status orthrus_step_noalloc(orthrus_engine *eng, const orthrus_batch *batch, const orthrus_pool_state *pool,
+                                    float *logits, int32_t logits_cap_rows, float *emb, int32_t emb_cap_rows,
+                                    int32_t *n_logits, int32_t *n_emb, int32_t *logit_req_ids,
+                                    int32_t *emb_req_ids, float *hidden_out, void *stream) {
+  return step_impl(eng, batch, pool, logits, logits_cap_rows, emb, emb_cap_rows, n_logits, n_emb, logit_req_ids,
+                   emb_req_ids, hidden_out, stream, true);
 }
 
 orthrus_status orthrus_set_layer_dump(orthrus_engine *eng, float *dst, int64_t cap_rows) {

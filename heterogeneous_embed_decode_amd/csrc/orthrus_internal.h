@@ -49,6 +49,18 @@ void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const
                      std::vector<AttnWork> &work, std::vector<DevItem> &items, int &n_chunk,
                      int &n_parts);
 
+// ---- static scratch of the allocation-free step (scratch.hip) --------------
+// 64 MiB per device: the step metadata at the start (at most
+// NOALLOC_META_BYTES), the decode partial results after it.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+constexpr size_t NOALLOC_META_BYTES = size_t(4) << 20;
+// Resolve the scratch array's address on `device`, which must be the
+// current device; once per device, later calls return at once.  Returns a
+// hipError_t value.
+int noalloc_scratch_init(int device);
+// The resolved address on `device`, or nullptr before noalloc_scratch_init.
+void *noalloc_scratch(int device);
+
 // ---- kernel launchers (kernels_*.hip) -------------------------------------
 struct LoraArgs {
   const uint16_t *U = nullptr;   // [rows][ldu] bf16, already scaled

@@ -78,9 +78,10 @@ class DeviceModel:
     def step_args(self, batch):
         return BatchArgs(batch.items_array(), batch.token_ids, batch.page_ids)
 
-    def step(self, batch, want_hidden=False, stream=None, args=None):
+    def step(self, batch, want_hidden=False, stream=None, args=None, noalloc=False):
         """Launch one step; returns (status, n_logits, n_emb).  Outputs live in
-        self.logits[:n_logits], self.emb[:n_emb], self.hidden[:T]."""
+        self.logits[:n_logits], self.emb[:n_emb], self.hidden[:T].  noalloc:
+        through orthrus_step_noalloc."""
         a = args if args is not None else self.step_args(batch)
         if stream is None:
             stream = torch.cuda.current_stream(self.device).cuda_stream
@@ -89,7 +90,8 @@ class DeviceModel:
                                   self.logits.shape[0], self.emb.data_ptr(), self.emb.shape[0],
                                   self.hidden.data_ptr() if want_hidden else None, stream,
                                   self.logit_req, self.emb_req,
-                                  self.pool_buf.data_ptr() if self.pool_buf is not None else None, self.buf_rows)
+                                  self.pool_buf.data_ptr() if self.pool_buf is not None else None, self.buf_rows,
+                                  noalloc=noalloc)
         return st, nl, ne
 
     def step_checked(self, batch, want_hidden=False):

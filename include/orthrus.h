@@ -198,6 +198,30 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch,
                             int32_t *n_logits, int32_t *n_emb, int32_t *logit_req_ids,
                             int32_t *emb_req_ids, float *hidden_out, void *stream);
 
+/* orthrus_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, kernels and results as orthrus_step, but the step's
+ * metadata and its decode-attention partial results live in a static
+ * device array of 64 MiB that the library holds on every device it runs
+ * on from module load to process end (its address is resolved once per
+ * device by orthrus_create), and the call never calls hipMalloc, hipFree,
+ * hipHostMalloc or any allocating routine.  Limits: at most 4 MiB of step
+ * metadata (about 3 int32 words per row, the page ids, and 8 words per
+ * item and per attention work entry: one per 128/(Hq/Hkv) rows of a chunk
+ * per KV head, one per decode split per KV head) and 60 MiB of decode
+ * partial results ((Hq/Hkv) * (2 + head_dim) * 4 bytes per decode split
+ * per KV head; decode rows split their keys in pieces of 128 to 512);
+ * beyond either, ECAPACITY before any device work, with the limit in
+ * orthrus_last_error.  Every call on one device shares that device's
+ * array: calls that overlap on one device (two engines on two streams,
+ * or host threads) race and are not supported; calls in stream order are
+ * safe, since each call writes all the scratch it reads. */
+orthrus_status orthrus_step_noalloc(orthrus_engine *eng, const orthrus_batch *batch,
+                                    const orthrus_pool_state *pool, float *logits, int32_t logits_cap_rows,
+                                    float *emb, int32_t emb_cap_rows, int32_t *n_logits, int32_t *n_emb,
+                                    int32_t *logit_req_ids, int32_t *emb_req_ids, float *hidden_out,
+                                    void *stream);
+
 /* Message of the last failed call on this engine ("" if none).  With
  * eng == NULL: the message of the last orthrus_create that failed in this
  * process ("" if none); not synchronised between threads. */

@@ -1,0 +1,116 @@
+"""orthrus_step_noalloc (the allocation-free step, for callers that cannot
+allocate device memory) against orthrus_step through the C ABI: two
+engines with the same weights, KV pages and pooling state run the same two
+batches in a row, the second smaller than the first, one engine through
+each entry point.  Both run the same kernels, so KV pages agree bit for
+bit and the hidden states and logits within the step's own run-to-run
+spread: rows whose residual projections end in atomically summed partial
+tiles differ in the last fp32 bit between any two runs, and where that
+flips a bf16 rounding of the FFN input the SwiGLU output's roundings
+amplify it to about 1e-3 on a few rows (two orthrus_step engines differ
+the same way).  So every row is held to the parity bar (2e-2) and the
+median row to 1e-5; stale metadata or partial results of the first call
+read by the second would break both.  A batch whose decode partial
+results exceed the static scratch is refused before any device work."""
+
+import numpy as np
+import pytest
+import torch
+
+import heterogeneous_embed_decode_amd as hed
+from heterogeneous_embed_decode_amd.device_model import DeviceModel
+from synth import model as sm
+from synth import workloads as wl
+from tests._util import row_rel_l2, cosine
+
+pytestmark = pytest.mark.gpu
+
+
+def _pair(cfg, n_pages, bits, kv):
+    a = DeviceModel(cfg, bits, n_pages, max_tokens=8192, max_items=1024, max_pool_slots=16, kv_bits=kv)
+    b = DeviceModel(cfg, bits, n_pages, max_tokens=8192, max_items=1024, max_pool_slots=16, kv_bits=kv)
+    rng = np.random.default_rng(5)
+    for t in ("pool_sum", "pool_kept"):
+        v = torch.from_numpy(rng.standard_normal(getattr(a, t).shape).astype(np.float32))
+        getattr(a, t).copy_(v)
+        getattr(b, t).copy_(v)
+    w = torch.from_numpy(rng.integers(1, 300, a.pool_wsum.shape[0]).astype(np.float32))
+    a.pool_wsum.copy_(w)
+    b.pool_wsum.copy_(w)
+    return a, b
+
+
+def _compare(a, b, batch, tag):
+    print(f"[no-alloc {tag}] items={batch.n_items} rows={batch.n_tokens}", flush=True)
+    sa = a.step(batch, want_hidden=True)
+    sb = b.step(batch, want_hidden=True, noalloc=True)
+    assert sa[0] == hed.OK, hed.orthrus_last_error(a.eng)
+    assert sb[0] == hed.OK, hed.orthrus_last_error(b.eng)
+    assert sa[1:] == sb[1:]
+    torch.cuda.synchronize()
+    nl, ne, T = sa[1], sa[2], batch.n_tokens
+    h = row_rel_l2(b.hidden[:T].cpu().numpy(), a.hidden[:T].cpu().numpy())
+    res = {"hidden_row_max": float(h.max()), "hidden_row_median": float(np.median(h)),
+           "rows_above_1e-5": int((h > 1e-5).sum())}
+    assert h.max() < 2e-2, (tag, res)
+    assert np.median(h) < 1e-5, (tag, res)
+    if nl:
+        lg = row_rel_l2(b.logits[:nl].cpu().numpy(), a.logits[:nl].cpu().numpy())
+        res["logit_row_max"] = float(lg.max())
+        assert lg.max() < 2e-2, (tag, res)
+        assert np.median(lg) < 1e-5 or nl < 8, (tag, res)
+        assert np.array_equal(a.logit_req[:nl], b.logit_req[:nl])
+    if ne:
+        ea, eb = a.emb[:ne].cpu().numpy(), b.emb[:ne].cpu().numpy()
+        res["emb_cos_min"] = min(cosine(ea[i], eb[i]) for i in range(ne))
+        assert res["emb_cos_min"] > 1 - 1e-6, (tag, res)
+        assert np.array_equal(a.emb_req[:ne], b.emb_req[:ne])
+    assert torch.equal(a.K, b.K) and torch.equal(a.V, b.V), (tag, "KV pages")
+    assert torch.equal(a.pool_wsum, b.pool_wsum), (tag, "weight totals")
+    for t in ("pool_sum", "pool_kept"):
+        e = row_rel_l2(getattr(b, t).cpu().numpy(), getattr(a, t).cpu().numpy())
+        res[t + "_row_max"] = float(e.max())
+        assert e.max() < 2e-2, (tag, t, res)
+    print(f"[no-alloc {tag}] {res}", flush=True)
+
+
+def test_noalloc_matches_step_two_calls():
+    cfg, big, n_pages = wl.one_layer_workload()
+    bits = sm.make_weights(cfg, seed=0)
+    kv = wl.synthetic_kv(cfg, n_pages, seed=3)
+    a, b = _pair(cfg, n_pages, bits, kv)
+    # first call: 4160 rows, 64 decode rows split into many partial results
+    _compare(a, b, big, "one-layer batch")
+    # second call: a smaller ragged batch (fewer rows, items and partials)
+    small, _ = wl.random_batch(cfg, 31, max_items=12, max_len=200, max_ctx=1500, n_pages=n_pages)
+    assert small.n_tokens < big.n_tokens
+    _compare(a, b, small, "smaller ragged batch")
+    a.close()
+    b.close()
+
+
+def test_noalloc_refuses_partials_beyond_scratch():
+    """600 decode rows at context 3500 need 600 x 8 x 7 partial results of
+    4 x 130 fp32 values (70 MB), beyond the 60 MiB partial area: ECAPACITY,
+    nothing launched.  The rows share their first 218 pages (read only) and
+    each has its own last page, where its new token would go."""
+    cfg = sm.MISTRAL_7B.with_(n_layers=1)
+    ps, shared, n_dec = cfg.page_size, 218, 600
+    n_pages = shared + n_dec
+    assert shared * ps <= 3500 < (shared + 1) * ps
+    bits = sm.make_weights(cfg, seed=0)
+    dev = DeviceModel(cfg, bits, n_pages, max_tokens=1024, max_items=1024, max_pool_slots=4)
+    items, pages = [], []
+    for i in range(n_dec):
+        items.append(wl.Item(kind=wl.DECODE, req_id=i, n_tokens=1, ctx_len=3500, page_off=len(pages),
+                             n_pages=shared + 1))
+        pages.extend(range(shared))
+        pages.append(shared + i)
+    batch = wl.Batch(items, np.ones(n_dec, np.int32), np.asarray(pages, np.int32))
+    before = dev.K.clone()
+    st, _, _ = dev.step(batch, noalloc=True)
+    assert st == hed.ECAPACITY
+    assert "partial" in hed.orthrus_last_error(dev.eng)
+    torch.cuda.synchronize()
+    assert torch.equal(before, dev.K)
+    dev.close()
