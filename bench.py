@@ -297,6 +297,9 @@ def main():
     ap.add_argument("--sampler-only", action="store_true",
                     help="run one step of the workload, then time only the sampler on its logit rows "
                          "(temperature 0.8, top-p 0.9); prints the sampler object")
+    ap.add_argument("--counters", action="store_true",
+                    help="run only --warmup + --steps steps of the workload and exit (for rocprofv3 counter "
+                         "passes; no JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB (read) into 1 GiB (write), 5 times; "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -384,6 +387,12 @@ def main():
                 raise hed.OrthrusError(s, hed.orthrus_last_error(dev.eng))
             rows_done[0] += batches[j].n_tokens
 
+    if args.counters:
+        run(args.warmup + args.steps)
+        torch.cuda.synchronize()
+        print(f"ran {args.warmup + args.steps} steps", file=sys.stderr, flush=True)
+        dev.close()
+        return
     if args.sampler_only:
         print(json.dumps({"sampler": measure_sampler(dev, cfg, meta, stream, run, greedy_too=False)}), flush=True)
         dev.close()
