@@ -69,6 +69,7 @@ def kernel_work(cfg, batch, meta):
         "lm_head": (2.0 * G * V * d, 2.0 * (G * d + V * d) + 4.0 * G * V),
         "attn_chunk": (chunk_flops, chunk_bytes),
         "attn_decode": (dec_flops, dec_bytes),
+        "attn_ragged": (chunk_flops + dec_flops, chunk_bytes + dec_bytes),
         "lora_shrink_qkv": (2.0 * TE * 3 * r * d, 2.0 * (TE * d + 3 * r * d)),
         "lora_shrink_o": (2.0 * TE * r * qd, 2.0 * (TE * qd + r * qd)),
         "pool": (0.0, pool_bytes(cfg, batch)),
@@ -119,6 +120,22 @@ def host_description():
     except Exception:
         pass
     return {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas": blas}
+
+
+def decode_only(batch):
+    """The decode items of a batch as a batch of their own (page lists
+    re-based), for timing decode attention alone."""
+    from synth import workloads as wl
+    items, toks, pages = [], [], []
+    t = 0
+    for i, it in enumerate(batch.items):
+        if it.kind == wl.DECODE:
+            items.append(wl.Item(**{**it.__dict__, "page_off": len(pages)}))
+            pages.extend(batch.item_pages(i).tolist())
+            toks.append(int(batch.token_ids[t]))
+        t += it.n_tokens
+    import numpy as np
+    return wl.Batch(items, np.asarray(toks, np.int32), np.asarray(pages, np.int32))
 
 
 def pool_bytes(cfg, batch):
@@ -297,6 +314,8 @@ def main():
     ap.add_argument("--sampler-only", action="store_true",
                     help="run one step of the workload, then time only the sampler on its logit rows "
                          "(temperature 0.8, top-p 0.9); prints the sampler object")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="with --counters: run only the decode items of each step (decode attention alone)")
     ap.add_argument("--counters", action="store_true",
                     help="run only --warmup + --steps steps of the workload and exit (for rocprofv3 counter "
                          "passes; no JSON line)")
@@ -388,6 +407,9 @@ def main():
             rows_done[0] += batches[j].n_tokens
 
     if args.counters:
+        if args.decode_only:
+            batches[:] = [decode_only(b) for b in batches]
+            bargs[:] = [dev.step_args(b) for b in batches]
         run(args.warmup + args.steps)
         torch.cuda.synchronize()
         print(f"ran {args.warmup + args.steps} steps", file=sys.stderr, flush=True)
@@ -469,12 +491,36 @@ def main():
     roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic,
             "algorithmic_per_launch": fl if bound == "mfma" else by, "avg_ms": round(avg_s * 1e3, 5)}
-    # decode attention is the HBM-bound part of the path: report its bandwidth too
-    if "attn_decode" in prof:
-        a_avg = prof["attn_decode"]["total_ms"] / prof["attn_decode"]["count"] * 1e-3
-        roof["attn_decode_hbm_gbs"] = round(work["attn_decode"][1] / a_avg / 1e9, 1)
-        roof["attn_decode_hbm_frac"] = round(work["attn_decode"][1] / a_avg / 1e9 / PEAK_HBM_GBS, 4)
-        roof["attn_decode_traffic"] = traffic_from_profiles("attn_decode", args.workload)
+    # ragged attention runs chunk tiles (matrix-bound) and decode splits
+    # (HBM-bound) in one launch: its fraction is the sum of both terms over
+    # its time
+    if "attn_ragged" in prof:
+        r_avg = prof["attn_ragged"]["total_ms"] / prof["attn_ragged"]["count"] * 1e-3
+        t_r = work["attn_chunk"][0] / (PEAK_BF16_TFLOPS * 1e12) + work["attn_decode"][1] / (PEAK_HBM_GBS * 1e9)
+        roof["attn_ragged_frac"] = round(t_r / r_avg, 4)
+    # decode attention is the HBM-bound part of the path: its bandwidth, timed
+    # on the same steps' decode rows alone
+    dec_batches = [decode_only(b) for b in batches]
+    if any(b.n_items for b in dec_batches):
+        dargs = [dev.step_args(b) for b in dec_batches]
+        for j, b in enumerate(dec_batches):
+            s_, _, _ = dev.step(b, stream=sptr, args=dargs[j])
+            assert s_ == hed.OK
+        torch.cuda.synchronize()
+        hed.orthrus_profile(dev.eng, True)
+        for _ in range(max(1, args.steps // len(dec_batches))):
+            for j, b in enumerate(dec_batches):
+                s_, _, _ = dev.step(b, stream=sptr, args=dargs[j])
+                assert s_ == hed.OK
+        torch.cuda.synchronize()
+        dprof = hed.orthrus_profile_read(dev.eng)
+        hed.orthrus_profile(dev.eng, False)
+        d_avg = dprof["attn_ragged"]["total_ms"] / dprof["attn_ragged"]["count"] * 1e-3
+        d_bytes = sum(kernel_work(cfg, b, m)["attn_decode"][1] for b, m in zip(batches, metas)) / len(batches)
+        roof["attn_decode_hbm_gbs"] = round(d_bytes / d_avg / 1e9, 1)
+        roof["attn_decode_hbm_frac"] = round(d_bytes / d_avg / 1e9 / PEAK_HBM_GBS, 4)
+        roof["attn_decode_avg_ms"] = round(d_avg * 1e3, 5)
+        roof["attn_decode_traffic"] = traffic_from_profiles("attn_ragged_decode", args.workload)
 
     sampler = measure_sampler(dev, cfg, meta, stream, run)
     cpu = None

@@ -1,6 +1,7 @@
-// Ragged causal attention over the paged KV cache: a chunk kernel for
-// embedding and prefill chunks, a decode kernel for single-row items, and
-// the log-sum-exp combine of decode splits.
+// Ragged causal attention over the paged KV cache: one launch over a work
+// list that mixes chunk tiles (embedding and prefill chunks) and decode
+// splits (single-row items), then the log-sum-exp combine of the decode
+// rows whose keys were split.
 //
 // Efficient Iterative Retrieval with Heterogeneous Batching: §3.2 Batch
 // Unit (embedding chunks, prefill chunks and decode rows share one pass and
@@ -17,8 +18,8 @@
 //           staged in LDS; P^T stays in registers and O^T = V^T P^T reads a
 //           transposed V tile from LDS.  Online softmax in fp32 (exp2).
 //  DECODE : one decode row, one KV head, one split of its keys.  Head dims
-//           64 and 128: each wave streams 16-key blocks with the next
-//           block's loads in flight; S^T = K Q^T on 16x16x32 bf16 MFMAs
+//           64 and 128: each wave streams 16-key blocks with the loads of
+//           its next RING-1 blocks in flight; S^T = K Q^T on 16x16x32 bf16 MFMAs
 //           (the grouped query heads are the 16 columns), P passes through
 //           LDS to the V layout and P.V runs as packed bf16 dot products
 //           over key pairs.  Head dims 16 and 32: each wave loads its 32
@@ -28,6 +29,8 @@
 //           split covers the whole context.
 #include "device_common.h"
 #include "orthrus_internal.h"
+
+#include <type_traits>
 
 namespace orthrus {
 
@@ -491,7 +494,7 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int HD, int G>
+template <int HD, int G, int RING>
 __device__ void decode_mfma_path(const AttnArgs &a, const AttnWork &w, DecodeMfmaSmem<HD, G> &sm) {
   static_assert(HD == 64 || HD == 128, "head dim");
   constexpr int LPK = HD / 8;   // lanes per key row in the V layout
@@ -606,17 +609,23 @@ __device__ void decode_mfma_path(const AttnArgs &a, const AttnWork &w, DecodeMfm
     }
     wave_lds_sync();  // the slot is rewritten by the next block
   };
-  u32x4_t kb[2][NJ], vb[2][NL];
+  // a ring of RING blocks in registers: RING-1 blocks in flight while one
+  // is consumed (the wave takes blocks wave, wave + 4, ...)
+  u32x4_t kb[RING][NJ], vb[RING][NL];
   int b = wave;
-  if (b < nblk) issue(b, kb[0], vb[0]);
+#pragma unroll
+  for (int r = 0; r < RING - 1; ++r)
+    if (b + r * ATTN_WAVES < nblk) issue(b + r * ATTN_WAVES, kb[r], vb[r]);
   while (b < nblk) {
-    if (b + ATTN_WAVES < nblk) issue(b + ATTN_WAVES, kb[1], vb[1]);
-    consume(b, kb[0], vb[0]);
-    b += ATTN_WAVES;
-    if (b >= nblk) break;
-    if (b + ATTN_WAVES < nblk) issue(b + ATTN_WAVES, kb[0], vb[0]);
-    consume(b, kb[1], vb[1]);
-    b += ATTN_WAVES;
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      if (b < nblk) {
+        const int nb = b + (RING - 1) * ATTN_WAVES;
+        if (nb < nblk) issue(nb, kb[(r + RING - 1) % RING], vb[(r + RING - 1) % RING]);
+        consume(b, kb[r], vb[r]);
+      }
+      b += ATTN_WAVES;
+    }
   }
   // totals over the lane groups, then stage this wave's record
   float lt = l_part + __shfl_xor(l_part, 16, 64);
@@ -644,24 +653,28 @@ __device__ void decode_mfma_path(const AttnArgs &a, const AttnWork &w, DecodeMfm
   finish_decode<HD, G>(a, w, it, sm.o, sm.ml);
 }
 
-template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) ChunkSmem<HD> sm;
-  chunk_path<HD>(a, a.work[blockIdx.x], sm);
-}
+// One launch over the whole work list: each workgroup runs the chunk path
+// or the decode path of its entry, so the HBM-bound decode splits and the
+// matrix-bound chunk tiles of one step share the chip.  The launch takes the
+// chunk path's registers and LDS (two workgroups per CU at head dim 128);
+// the decode path uses the spare registers for a 4-block load ring (2 where
+// 8 grouped heads at head dim 128 leave no room).
+template <int HD, int G>
+union RaggedSmem {
+  ChunkSmem<HD> c;
+  typename std::conditional<(HD >= 64), DecodeMfmaSmem<HD, G>, DecodeSmem<HD, G>>::type d;
+};
 
 template <int HD, int G>
-__global__ __launch_bounds__(256, 4) void attn_decode_vec_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) DecodeSmem<HD, G> sm;
-  decode_path<HD, G>(a, a.work[blockIdx.x], sm);
-}
-
-// eight grouped heads at head dim 128 need 64 accumulators per lane: two
-// workgroups per CU instead of three keeps them out of scratch
-template <int HD, int G>
-__global__ __launch_bounds__(256, (HD == 128 && G == 8) ? 2 : 3) void attn_decode_mfma_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) DecodeMfmaSmem<HD, G> sm;
-  decode_mfma_path<HD, G>(a, a.work[blockIdx.x], sm);
+__global__ __launch_bounds__(256, 2) void attn_ragged_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) RaggedSmem<HD, G> sm;
+  const AttnWork w = a.work[blockIdx.x];
+  if (w.type == WORK_CHUNK) {
+    chunk_path<HD>(a, w, sm.c);
+  } else {
+    if constexpr (HD >= 64) decode_mfma_path<HD, G, (HD == 128 && G == 8) ? 2 : 4>(a, w, sm.d);
+    else decode_path<HD, G>(a, w, sm.d);
+  }
 }
 
 // Merge the split partials of each decode row: out = sum_p 2^(m_p - M) o_p /
@@ -749,48 +762,20 @@ static AttnArgs attn_args(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, c
   return a;
 }
 
-int launch_attn_chunk(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
-                      const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
-                      uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps, void *stream) {
-  if (n_work <= 0) return 0;
-  const AttnArgs a = attn_args(qkv, ld_qkv, kc, vc, page_ids, items, work, nullptr, nullptr, o, ld_o, Hq, Hkv,
-                               hd, ps);
-  hipStream_t s = (hipStream_t)stream;
-  switch (hd) {
-    case 16: hipLaunchKernelGGL(attn_chunk_kernel<16>, dim3(n_work), dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL(attn_chunk_kernel<32>, dim3(n_work), dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(attn_chunk_kernel<64>, dim3(n_work), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(attn_chunk_kernel<128>, dim3(n_work), dim3(256), 0, s, a); break;
-    default: return (int)hipErrorInvalidValue;
-  }
-  ORTHRUS_LAUNCH_CHECK();
-  return 0;
-}
-
-template <int HD, int G>
-static void launch_decode_g(const AttnArgs &a, int n_work, hipStream_t s) {
-  if constexpr (HD >= 64)
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<HD, G>), dim3(n_work), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_decode_vec_kernel<HD, G>), dim3(n_work), dim3(256), 0, s, a);
-}
-
 template <int HD>
-static int launch_decode_hd(const AttnArgs &a, int n_work, int G, hipStream_t s) {
+static int launch_ragged_hd(const AttnArgs &a, int n_work, int G, hipStream_t s) {
   switch (G) {
-    case 1: launch_decode_g<HD, 1>(a, n_work, s); break;
-    case 2: launch_decode_g<HD, 2>(a, n_work, s); break;
-    case 4: launch_decode_g<HD, 4>(a, n_work, s); break;
-    case 8: launch_decode_g<HD, 8>(a, n_work, s); break;
+    case 1: hipLaunchKernelGGL((attn_ragged_kernel<HD, 1>), dim3(n_work), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_ragged_kernel<HD, 2>), dim3(n_work), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_ragged_kernel<HD, 4>), dim3(n_work), dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((attn_ragged_kernel<HD, 8>), dim3(n_work), dim3(256), 0, s, a); break;
     default: return (int)hipErrorInvalidValue;
   }
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }
 
-int decode_split_limit(int hd) { return hd >= 64 ? DEC_SPLIT_MAX : DEC_SPLIT_VEC; }
-
-int launch_attn_decode(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
+int launch_attn_ragged(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
                        const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
                        float *part_ml, float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps,
                        void *stream) {
@@ -800,13 +785,15 @@ int launch_attn_decode(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, cons
   const int G = Hq / Hkv;
   hipStream_t s = (hipStream_t)stream;
   switch (hd) {
-    case 16: return launch_decode_hd<16>(a, n_work, G, s);
-    case 32: return launch_decode_hd<32>(a, n_work, G, s);
-    case 64: return launch_decode_hd<64>(a, n_work, G, s);
-    case 128: return launch_decode_hd<128>(a, n_work, G, s);
+    case 16: return launch_ragged_hd<16>(a, n_work, G, s);
+    case 32: return launch_ragged_hd<32>(a, n_work, G, s);
+    case 64: return launch_ragged_hd<64>(a, n_work, G, s);
+    case 128: return launch_ragged_hd<128>(a, n_work, G, s);
   }
   return (int)hipErrorInvalidValue;
 }
+
+int decode_split_limit(int hd) { return hd >= 64 ? DEC_SPLIT_MAX : DEC_SPLIT_VEC; }
 
 int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_dec, const float *part_ml,
                         const float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd,

@@ -84,13 +84,11 @@ int launch_rmsnorm(const float *x, const uint16_t *g, uint16_t *h, int T, int d,
 int launch_rope_kv(uint16_t *qkv, const int32_t *pos, const int32_t *slot,
                    const double *inv_freq, uint16_t *kc, uint16_t *vc, int T, int Hq, int Hkv,
                    int hd, int ps, void *stream);
-int launch_attn_chunk(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
-                      const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
-                      uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps, void *stream);
-int launch_attn_decode(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
+// one launch over the work list (chunk entries first, then decode entries)
+int launch_attn_ragged(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
                        const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
-                       float *part_ml, float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd,
-                       int ps, void *stream);
+                       float *part_ml, float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps,
+                       void *stream);
 int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_dec,
                         const float *part_ml, const float *part_o, uint16_t *o, int ld_o,
                         int Hq, int Hkv, int hd, void *stream);
