@@ -42,9 +42,9 @@ def pages_needed(cfg, ctxs, extra_chunks=()):
 
 def expected_split(cfg, ctxs):
     """The split the library picks: the largest of 512/256/128 keys that
-    still gives 4096 decode workgroups."""
+    still gives 2048 decode workgroups."""
     split = 512 if cfg.head_dim >= 64 else 128
-    while split > 128 and cfg.n_kv_heads * sum((int(c) + split) // split for c in ctxs) < 4096:
+    while split > 128 and cfg.n_kv_heads * sum((int(c) + split) // split for c in ctxs) < 2048:
         split //= 2
     return split
 
@@ -69,12 +69,12 @@ CASES = [
     ("hd64-g2-ps32-split256",
      sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=4, head_dim=64, ffn_dim=256,
                     vocab=300, page_size=32, rope_theta=1e4),
-     list(np.random.default_rng(4).integers(200, 1200, 320)),
+     list(np.random.default_rng(4).integers(200, 1200, 160)),
      [(64, 0), (33, 700)]),
     ("hd128-g1-ps16-split256",
      sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=4, head_dim=128, ffn_dim=256,
                     vocab=300, page_size=16, rope_theta=1e6),
-     list(np.random.default_rng(5).integers(100, 1000, 400)),
+     list(np.random.default_rng(5).integers(100, 1000, 200)),
      []),
     ("hd128-g2-ps5-split128",
      sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=128, ffn_dim=256,
