@@ -20,6 +20,7 @@ STATUS_NAMES = ["OK", "EINVAL", "ENOPAGES", "ECAPACITY", "ESTATE", "ENOMEM", "EH
 EMBED, PREFILL, DECODE = 0, 1, 2
 POOL_MEAN, POOL_WMEAN, POOL_CLS, POOL_LAST = 0, 1, 2, 3
 EPI_BF16, EPI_F32, EPI_RESID, EPI_SWIGLU = 0, 1, 2, 3
+DTYPE_BF16, DTYPE_F32 = 0, 1
 
 _i32 = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -30,7 +31,8 @@ class orthrus_model_cfg(ctypes.Structure):
     _fields_ = [(n, _i32) for n in (
         "n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
         "lora_rank", "page_size", "n_pages", "max_tokens", "max_items", "max_pool_slots")] + [
-        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("lora_scale", ctypes.c_float)]
+        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("lora_scale", ctypes.c_float),
+        ("dtype", _i32)]
 
 
 class orthrus_layer_w(ctypes.Structure):
@@ -138,10 +140,10 @@ class OrthrusError(RuntimeError):
 
 def make_cfg(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, lora_rank,
              page_size, n_pages, max_tokens, max_items, max_pool_slots, rope_theta, rms_eps,
-             lora_scale) -> orthrus_model_cfg:
+             lora_scale, dtype=DTYPE_BF16) -> orthrus_model_cfg:
     return orthrus_model_cfg(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab,
                              lora_rank, page_size, n_pages, max_tokens, max_items, max_pool_slots,
-                             rope_theta, rms_eps, lora_scale)
+                             rope_theta, rms_eps, lora_scale, dtype)
 
 
 class BatchArgs:

@@ -26,7 +26,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 SOURCES = ["pack.cpp", "engine.cpp", "sched.cpp", "kernels_gemm.hip", "kernels_attn.hip", "kernels_misc.hip",
-           "kernels_sample.hip", "scratch.hip"]
+           "kernels_sample.hip", "scratch.hip", "kernels_f32.hip"]
 
 
 def _compile(src: str) -> str:

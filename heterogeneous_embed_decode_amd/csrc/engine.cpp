@@ -195,6 +195,7 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
       c.ffn_dim < 8 || c.page_size < 1 || c.n_pages < 1 || c.max_tokens < 1 || c.max_items < 1 ||
       c.max_pool_slots < 0 || c.lora_rank < 0)
     return ORTHRUS_EINVAL;
+  if (c.dtype != ORTHRUS_BF16 && c.dtype != ORTHRUS_F32) return ORTHRUS_EINVAL;
   if (!(hd == 16 || hd == 32 || hd == 64 || hd == 128)) return ORTHRUS_EINVAL;
   if (c.n_q_heads % c.n_kv_heads) return ORTHRUS_EINVAL;
   const int G = c.n_q_heads / c.n_kv_heads;
@@ -238,18 +239,19 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
     return bail(ORTHRUS_EHIP, "hipGetSymbolAddress(scratch)", r);
   const size_t T = c.max_tokens, d = c.d_model;
   const size_t qkvd = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * hd, qd = (size_t)c.n_q_heads * hd;
+  const size_t es = c.dtype == ORTHRUS_F32 ? 4 : 2;  // bytes of an activation element
   struct {
     void **p;
     size_t bytes;
   } allocs[] = {
       {(void **)&eng->x, T * d * 4},
-      {(void **)&eng->h, T * std::max(d, qd) * 2},
-      {(void **)&eng->qkv, T * qkvd * 2},
-      {(void **)&eng->o, T * qd * 2},
-      {(void **)&eng->act, T * (size_t)c.ffn_dim * 2},
-      {(void **)&eng->U, T * (size_t)std::max(3 * c.lora_rank, 8) * 2},
+      {(void **)&eng->h, T * std::max(d, qd) * es},
+      {(void **)&eng->qkv, T * qkvd * es},
+      {(void **)&eng->o, T * qd * es},
+      {(void **)&eng->act, T * (size_t)c.ffn_dim * es},
+      {(void **)&eng->U, T * (size_t)std::max(3 * c.lora_rank, 8) * es},
       {(void **)&eng->hf, T * d * 4},
-      {(void **)&eng->hl, T * d * 2},
+      {(void **)&eng->hl, T * d * es},
       {(void **)&eng->inv_freq, (size_t)hd / 2 * 8},
   };
   for (auto &a : allocs)
@@ -390,6 +392,7 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
   const size_t o_items = off; off = align4(off + eng->items.size() * 8);
   const size_t o_work = off; off = align4(off + eng->work.size() * 8);
   const size_t o_norm = off; off = align4(off + norm_rows.size());
+  const size_t o_ritem = off; off = align4(off + (c.dtype == ORTHRUS_F32 ? (size_t)T : 0));
   const size_t words = std::max<size_t>(off, 4);
   const int Gq = c.n_q_heads / c.n_kv_heads;
   int32_t *meta_dev = eng->meta_dev;
@@ -467,6 +470,7 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
   if (!eng->items.empty()) memcpy(mh + o_items, eng->items.data(), eng->items.size() * 32);
   if (!eng->work.empty()) memcpy(mh + o_work, eng->work.data(), eng->work.size() * 32);
   if (!norm_rows.empty()) memcpy(mh + o_norm, norm_rows.data(), norm_rows.size() * 4);
+  if (c.dtype == ORTHRUS_F32) memcpy(mh + o_ritem, p.row_item.data(), (size_t)T * 4);
   if (eng->done_pending && eng->last_stream != s)
     HIPCHK(hipStreamWaitEvent(s, eng->done, 0), "hipStreamWaitEvent");
   HIPCHK(hipMemcpyAsync(meta_dev, mh, words * 4, hipMemcpyHostToDevice, s), "metadata upload");
@@ -485,6 +489,59 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
   const int TE = p.rows_by_kind[0];
   const size_t layer_kv = (size_t)c.n_pages * Hkv * c.page_size * hd;
 
+  if (c.dtype == ORTHRUS_F32) {
+    // fp32 path: the same forward on fp32 weights, pages and activations
+    float *h = (float *)eng->h, *qkv = (float *)eng->qkv, *o = (float *)eng->o, *act = (float *)eng->act;
+    float *U = (float *)eng->U, *hl = (float *)eng->hl;
+    const int32_t *d_ritem = meta_dev + o_ritem;
+    for (int l = 0; l < c.n_layers; ++l) {
+      const orthrus_layer_w &L = eng->layers[l];
+      float *kc = (float *)eng->kc + (size_t)l * layer_kv, *vc = (float *)eng->vc + (size_t)l * layer_kv;
+      const bool lora = r > 0 && TE > 0;
+      LCHK(launch_rmsnorm_f32(l == 0 ? d_tok : nullptr, (const float *)eng->w.tok_emb, eng->x,
+                              (const float *)L.g_attn, h, T, d, c.rms_eps, s),
+           "rmsnorm_f32");
+      if (lora)
+        LCHK(launch_gemm_f32(h, d, (const float *)L.lora_a_qkv, d, U, 3 * r, TE, 3 * r, d, EPI_F32, 0,
+                             c.lora_scale, nullptr, 0, nullptr, 0, 0, 0, 0, s),
+             "lora_shrink_qkv_f32");
+      LCHK(launch_gemm_f32(h, d, (const float *)L.w_qkv, d, qkv, qkvd, T, qkvd, d, EPI_F32, 0, 1.f,
+                           lora ? U : nullptr, 3 * r, (const float *)L.lora_b_qkv, r, TE, qd, qd + kvd, s),
+           "gemm_qkv_f32");
+      LCHK(launch_rope_kv_f32(qkv, d_pos, d_slot, eng->inv_freq, kc, vc, T, Hq, Hkv, hd, c.page_size, s),
+           "rope_kv_f32");
+      LCHK(launch_attn_f32(qkv, kc, vc, d_pages, d_items, d_ritem, d_pos, o, T, Hq, Hkv, hd, c.page_size, s),
+           "attn_f32");
+      if (lora)
+        LCHK(launch_gemm_f32(o, qd, (const float *)L.lora_a_o, qd, U, r, TE, r, qd, EPI_F32, 0, c.lora_scale,
+                             nullptr, 0, nullptr, 0, 0, 0, 0, s),
+             "lora_shrink_o_f32");
+      LCHK(launch_gemm_f32(o, qd, (const float *)L.w_o, qd, eng->x, d, T, d, qd, EPI_RESID, 0, 1.f,
+                           lora ? U : nullptr, r, (const float *)L.lora_b_o, r, TE, d, d, s),
+           "gemm_o_f32");
+      LCHK(launch_rmsnorm_f32(nullptr, nullptr, eng->x, (const float *)L.g_ffn, h, T, d, c.rms_eps, s),
+           "rmsnorm_f32");
+      LCHK(launch_gemm_f32(h, d, (const float *)L.w_gate_up, d, act, F, T, F, d, EPI_SWIGLU, F, 1.f, nullptr, 0,
+                           nullptr, 0, 0, 0, 0, s),
+           "gemm_gate_up_f32");
+      LCHK(launch_gemm_f32(act, F, (const float *)L.w_down, F, eng->x, d, T, d, F, EPI_RESID, 0, 1.f, nullptr,
+                           0, nullptr, 0, 0, 0, 0, s),
+           "gemm_down_f32");
+      if (eng->dump)
+        HIPCHK(hipMemcpyAsync(eng->dump + (size_t)l * eng->dump_cap * d, eng->x, (size_t)T * d * 4,
+                              hipMemcpyDeviceToDevice, s),
+               "layer dump copy");
+    }
+    if (hidden_out)
+      HIPCHK(hipMemcpyAsync(hidden_out, eng->x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s), "hidden copy");
+    LCHK(launch_final_norm_f32(eng->x, (const float *)eng->w.g_final, d_logit, TE, G, eng->hf, hl, d, c.rms_eps,
+                               s),
+         "final_norm_f32");
+    if (G > 0)
+      LCHK(launch_gemm_f32(hl, d, (const float *)eng->w.lm_head, d, logits, c.vocab, G, c.vocab, d, EPI_F32, 0,
+                           1.f, nullptr, 0, nullptr, 0, 0, 0, 0, s),
+           "lm_head_f32");
+  } else {
   for (int l = 0; l < c.n_layers; ++l) {
     const orthrus_layer_w &L = eng->layers[l];
     uint16_t *kc = eng->kc + (size_t)l * layer_kv, *vc = eng->vc + (size_t)l * layer_kv;
@@ -544,6 +601,7 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
     LCHK(launch_gemm(eng->hl, d, (const uint16_t *)eng->w.lm_head, d, logits, c.vocab, G, c.vocab, d, EPI_F32,
                      0, 1.f, nullptr, s),
          "lm_head");
+  }
   if (n_segs) {
     bool any_l2 = false;  // an emitted embedding is scaled to unit length
     for (size_t q = 0; q < n_segs; ++q) any_l2 |= (p.pool_segs[q * 8 + 3] & ORTHRUS_POOL_L2) && p.pool_segs[q * 8 + 5];

@@ -94,6 +94,19 @@ int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_de
                         int Hq, int Hkv, int hd, void *stream);
 int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_rows, const int32_t *emb_rows,
                       int n_embed, int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream);
+// fp32 path (kernels_f32.hip)
+int launch_gemm_f32(const float *A, int lda, const float *B, int ldb, float *C, int ldc, int M, int N, int K,
+                    int epi, int b_up_row, float alpha, const float *U, int ldu, const float *Bx, int r, int lrows,
+                    int sec1, int sec2, void *stream);
+int launch_rmsnorm_f32(const int32_t *tok, const float *E, float *x, const float *g, float *h, int T, int d,
+                       float eps, void *stream);
+int launch_final_norm_f32(const float *x, const float *g, const int32_t *logit_rows, int n_embed, int n_logit,
+                          float *hf, float *hl, int d, float eps, void *stream);
+int launch_rope_kv_f32(float *qkv, const int32_t *pos, const int32_t *slot, const double *inv_freq, float *kc,
+                       float *vc, int T, int Hq, int Hkv, int hd, int ps, void *stream);
+int launch_attn_f32(const float *qkv, const float *kc, const float *vc, const int32_t *page_ids,
+                    const DevItem *items, const int32_t *row_item, const int32_t *pos, float *o, int T, int Hq,
+                    int Hkv, int hd, int ps, void *stream);
 int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, int nr, int K, float scale,
                        uint16_t *U, void *stream);
 int launch_sample(const float *logits, int64_t ld, int n_rows, int V, const float *temperature,

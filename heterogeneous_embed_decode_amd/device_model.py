@@ -8,24 +8,37 @@ import numpy as np
 import torch
 
 from . import (BatchArgs, make_cfg, orthrus_create, orthrus_step, orthrus_destroy,
-               orthrus_last_error, OrthrusError, OK)
+               orthrus_last_error, OrthrusError, OK, DTYPE_BF16, DTYPE_F32)
 
 _LAYER_KEYS = ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_ffn",
                "lora_a_qkv", "lora_b_qkv", "lora_a_o", "lora_b_o")
 
 
 def _dev_bits(a, device):
-    """uint16 bf16 bit patterns (numpy) -> device int16 tensor with the same bits."""
-    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
-    return t.to(device)
+    """uint16 bf16 bit patterns (numpy) -> device int16 tensor with the same
+    bits; float32 arrays (fp32 models) -> device float32 tensor."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return torch.from_numpy(a).to(device)
+    return torch.from_numpy(a.view(np.int16)).to(device)
+
+
+def _widen_bits(a):
+    """bf16 bit patterns -> float32 (exact), for fp32 models given bf16 data."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a
+    return (a.astype(np.uint32) << 16).view(np.float32)
 
 
 class DeviceModel:
     """Weights, KV pools and pooling state on one device plus an engine.
 
     dims: an object with n_layers, d_model, n_q_heads, n_kv_heads, head_dim,
-    ffn_dim, vocab, lora_rank, page_size, rope_theta, rms_eps, lora_scale.
-    weights: {name: uint16 array} (globals and 'layers.<l>.<name>').
+    ffn_dim, vocab, lora_rank, page_size, rope_theta, rms_eps, lora_scale and
+    optionally dtype ("bf16" or "f32").
+    weights: {name: uint16 bf16 bits, or float32 for an fp32 model} (globals
+    and 'layers.<l>.<name>').
     kv_bits: optional (K, V) uint16 arrays of the full pool shape
     [L, n_pages, Hkv, page_size, hd] to upload as prior KV content.
     """
@@ -35,16 +48,19 @@ class DeviceModel:
         self.dims = dims
         self.device = torch.device(device)
         torch.cuda.set_device(self.device)
-        self.w = {k: _dev_bits(v, self.device) for k, v in weights.items()}
+        self.f32 = getattr(dims, "dtype", "bf16") == "f32"
+        cast = _widen_bits if self.f32 else (lambda a: a)
+        self.w = {k: _dev_bits(cast(v), self.device) for k, v in weights.items()}
         shape = (dims.n_layers, n_pages, dims.n_kv_heads, dims.page_size, dims.head_dim)
+        kv_dtype = torch.float32 if self.f32 else torch.int16
         if kv_tensors is not None:
             self.K, self.V = kv_tensors
         elif kv_bits is not None:
-            self.K = _dev_bits(kv_bits[0], self.device).reshape(shape)
-            self.V = _dev_bits(kv_bits[1], self.device).reshape(shape)
+            self.K = _dev_bits(cast(kv_bits[0]), self.device).reshape(shape)
+            self.V = _dev_bits(cast(kv_bits[1]), self.device).reshape(shape)
         else:
-            self.K = torch.zeros(shape, dtype=torch.int16, device=self.device)
-            self.V = torch.zeros(shape, dtype=torch.int16, device=self.device)
+            self.K = torch.zeros(shape, dtype=kv_dtype, device=self.device)
+            self.V = torch.zeros(shape, dtype=kv_dtype, device=self.device)
         d = dims.d_model
         self.pool_sum = torch.zeros((max(max_pool_slots, 1), d), dtype=torch.float32, device=self.device)
         self.pool_wsum = torch.zeros(max(max_pool_slots, 1), dtype=torch.float32, device=self.device)
@@ -57,7 +73,7 @@ class DeviceModel:
         self.cfg = make_cfg(dims.n_layers, d, dims.n_q_heads, dims.n_kv_heads, dims.head_dim,
                             dims.ffn_dim, dims.vocab, dims.lora_rank, dims.page_size, n_pages,
                             max_tokens, max_items, max_pool_slots, dims.rope_theta, dims.rms_eps,
-                            dims.lora_scale)
+                            dims.lora_scale, DTYPE_F32 if self.f32 else DTYPE_BF16)
         layers = []
         for l in range(dims.n_layers):
             L = {}

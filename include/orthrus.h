@@ -20,7 +20,7 @@
  *  - bf16 is IEEE bfloat16 stored as 16-bit patterns; fp32 is IEEE binary32.
  *  - Linear weights are row-major [out_features][in_features].
  *  - K and V caches are each [n_layers][n_pages][n_kv_heads][page_size]
- *    [head_dim] bf16.  Token position p of an item lives in page
+ *    [head_dim] bf16 (fp32 for models of dtype ORTHRUS_F32).  Token position p of an item lives in page
  *    page_ids[page_off + p / page_size] at in-page offset p % page_size.
  *  - Nothing throws across this ABI.  Validation runs before any device
  *    work; on a non-OK status no device memory has been touched.
@@ -71,9 +71,19 @@ typedef struct {
   int32_t max_items;       /* largest item count the engine accepts */
   int32_t max_pool_slots;  /* rows of the pooling state arrays */
   float rope_theta, rms_eps, lora_scale;
+  int32_t dtype;           /* ORTHRUS_BF16 (0) or ORTHRUS_F32 (1), see below */
 } orthrus_model_cfg;
 
-/* Per-layer weights, all device bf16.
+/* Number format of a model (orthrus_model_cfg.dtype).  ORTHRUS_BF16: bf16
+ * weights and KV pages, bf16 matrix-core operands with fp32 accumulation,
+ * an fp32 residual stream, fp32 softmax and pooling.  ORTHRUS_F32: every
+ * weight, KV page, activation and accumulation in fp32 (weight and KV
+ * pointers then point to IEEE binary32 arrays of the same shapes), on
+ * kernels written for correctness at small sizes (the tiny fp32 decoder),
+ * not for speed. */
+enum { ORTHRUS_BF16 = 0, ORTHRUS_F32 = 1 };
+
+/* Per-layer weights, all device bf16 (fp32 when cfg.dtype is ORTHRUS_F32).
  *  w_qkv      [Hq*hd + 2*Hkv*hd][d]   q rows, then k rows, then v rows
  *  w_o        [d][Hq*hd]
  *  w_gate_up  [2*F][d]                gate rows, then up rows
@@ -88,7 +98,7 @@ typedef struct {
   const void *lora_a_qkv, *lora_b_qkv, *lora_a_o, *lora_b_o;
 } orthrus_layer_w;
 
-/* tok_emb [V][d], lm_head [V][d], g_final [d]: device bf16.
+/* tok_emb [V][d], lm_head [V][d], g_final [d]: device bf16 (fp32 for ORTHRUS_F32).
  * layers: host array of n_layers entries (copied by orthrus_create). */
 typedef struct {
   const void *tok_emb, *lm_head, *g_final;
@@ -160,7 +170,7 @@ orthrus_status orthrus_pack(const orthrus_model_cfg *cfg, const orthrus_batch *b
 /* Create an engine bound to the current HIP device.  Copies cfg and the
  * weight pointer table; allocates the workspace for max_tokens/max_items.
  * k_pages / v_pages: device bf16 KV pools (layout above), read and written
- * by every step.  Returns EINVAL for unsupported shapes (head_dim not in
+ * by every step.  Returns EINVAL for an unknown dtype or unsupported shapes (head_dim not in
  * {16,32,64,128}, n_q_heads not a multiple of n_kv_heads, d_model above
  * 8192, d_model, Hq*hd, ffn_dim not multiples of 8, lora_rank not a
  * multiple of 8, or a step operand of 2 GiB or more: max_tokens rows of

@@ -38,8 +38,10 @@ from .pooling import pool_item
 
 
 def widen_weights(bits: dict, dtype=np.float32) -> dict:
-    """bf16 bit patterns -> float arrays of ``dtype`` (exact widening)."""
-    return {k: bf16_bits_to_f32(v).astype(dtype) for k, v in bits.items()}
+    """bf16 bit patterns -> float arrays of ``dtype`` (exact widening); fp32
+    arrays (an fp32 model's weights) are taken as they are."""
+    return {k: (v.astype(dtype) if v.dtype == np.float32 else bf16_bits_to_f32(v).astype(dtype))
+            for k, v in bits.items()}
 
 
 def new_pool(n_slots: int, d: int, dtype=np.float32, buf_rows: int = 0) -> dict:

@@ -30,6 +30,7 @@ class ModelConfig:
     rope_theta: float = 1e4
     rms_eps: float = 1e-5
     lora_scale: float = 1.0
+    dtype: str = "bf16"      # number format of weights, KV and compute: "bf16" or "f32"
 
     @property
     def q_dim(self) -> int:
@@ -54,6 +55,9 @@ class ModelConfig:
 # heads of 16, SwiGLU 176, theta 1e4, vocab 256, KV pages of 8 tokens.
 TINY = ModelConfig(n_layers=2, d_model=64, n_q_heads=4, n_kv_heads=2, head_dim=16,
                    ffn_dim=176, vocab=256, lora_rank=0, page_size=8, rope_theta=1e4)
+
+# The same tiny decoder in fp32 (weights drawn in fp32, not rounded to bf16).
+TINY_F32 = TINY.with_(dtype="f32")
 
 # Mistral-7B shape: d 4096, 32 q / 8 kv heads of 128, SwiGLU 14336,
 # theta 1e6, vocab 32768 (the public Mistral-7B vocabulary size).
@@ -127,33 +131,55 @@ def normal_bf16(key, n: int, std: float, mean: float = 0.0) -> np.ndarray:
     return out
 
 
+def normal_f32(key, n: int, std: float, mean: float = 0.0) -> np.ndarray:
+    """As normal_bf16 (same generator and chunking), kept in fp32."""
+    out = np.empty(n, np.float32)
+    key = list(key)
+    for i in range((n + CHUNK - 1) // CHUNK):
+        m = min(CHUNK, n - i * CHUNK)
+        v = np.random.default_rng(key + [i]).standard_normal(m, dtype=np.float32)
+        v *= np.float32(std)
+        if mean:
+            v += np.float32(mean)
+        out[i * CHUNK: i * CHUNK + m] = v
+    return out
+
+
 def make_tensor(seed: int, name: str, shape, std: float = 0.02,
-                gain_std: float = 0.0) -> np.ndarray:
-    """One seeded tensor as uint16 bf16 bits."""
+                gain_std: float = 0.0, f32: bool = False) -> np.ndarray:
+    """One seeded tensor as uint16 bf16 bits (float32 values with f32)."""
     n = int(np.prod(shape)) if len(shape) else 1
     key = [_tensor_seed(seed, name)]
     base = name.split(".")[-1]
     if base.startswith("g_"):
         if not gain_std:
-            return f32_to_bf16_bits(np.ones(shape, np.float32))
+            ones = np.ones(shape, np.float32)
+            return ones if f32 else f32_to_bf16_bits(ones)
+        if f32:
+            return normal_f32(key, n, gain_std, mean=1.0).reshape(shape)
         return normal_bf16(key, n, gain_std, mean=1.0).reshape(shape)
+    if f32:
+        return normal_f32(key, n, std).reshape(shape)
     return normal_bf16(key, n, std).reshape(shape)
 
 
 def make_weights(cfg: ModelConfig, seed: int = 0, std: float = 0.02,
                  gain_std: float = 0.0, zero_lora_b: bool = False):
-    """All weights as {name: uint16 array}; layer tensors named 'layers.<l>.<n>'."""
+    """All weights as {name: uint16 bf16 bits}, or {name: float32} for a
+    model of dtype "f32"; layer tensors named 'layers.<l>.<n>'."""
     glob, layer = weight_shapes(cfg)
+    f32 = cfg.dtype == "f32"
+    zdt = np.float32 if f32 else np.uint16
     w = {}
     for n, s in glob.items():
-        w[n] = make_tensor(seed, n, s, std, gain_std)
+        w[n] = make_tensor(seed, n, s, std, gain_std, f32)
     for l in range(cfg.n_layers):
         for n, s in layer.items():
             full = f"layers.{l}.{n}"
             if n.startswith("lora_") and cfg.lora_rank == 0:
-                w[full] = np.zeros(s, np.uint16)
+                w[full] = np.zeros(s, zdt)
             elif n.startswith("lora_b") and zero_lora_b:
-                w[full] = np.zeros(s, np.uint16)
+                w[full] = np.zeros(s, zdt)
             else:
-                w[full] = make_tensor(seed, full, s, std, gain_std)
+                w[full] = make_tensor(seed, full, s, std, gain_std, f32)
     return w

@@ -145,3 +145,17 @@ def test_gemm_rejects_operands_of_2gib():
     assert hed.orthrus_gemm_bf16(8, 8192, 8, 8192, 8, big, 64, big, 8192, hed.EPI_BF16) == hed.EINVAL
     # residual C: 65536 x 8192 fp32 = 2 GiB (A and B are small)
     assert hed.orthrus_gemm_bf16(8, 64, 8, 64, 8, 8192, 65536, 8192, 64, hed.EPI_RESID) == hed.EINVAL
+
+
+def test_create_rejects_unknown_dtype_before_device_work():
+    """A model dtype other than bf16 (0) or fp32 (1) is refused by the
+    argument checks, before any HIP call (the pointers are never used)."""
+    from synth import model as sm
+    t = sm.TINY
+    for dt, want in ((2, hed.EINVAL), (-1, hed.EINVAL)):
+        cfg = hed.make_cfg(t.n_layers, t.d_model, t.n_q_heads, t.n_kv_heads, t.head_dim, t.ffn_dim, t.vocab,
+                           0, t.page_size, 16, 64, 8, 4, t.rope_theta, t.rms_eps, 1.0, dt)
+        layers = [{k: 8 for k in ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_ffn")}] * t.n_layers
+        with pytest.raises(hed.OrthrusError) as e:
+            hed.orthrus_create(cfg, 8, 8, 8, layers, 8, 8)
+        assert e.value.code == want
