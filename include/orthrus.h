@@ -51,8 +51,9 @@ enum { ORTHRUS_EMBED = 0, ORTHRUS_PREFILL = 1, ORTHRUS_DECODE = 2 };
 /* Pooling heads (§3.3 Incremental Pooler; agihunt summary).  MEAN weights
  * every token 1; WMEAN weights a token by its 1-based position in the
  * request; CLS keeps the hidden state at position 0; LAST keeps the hidden
- * state of the request's final token.  BUFFER (the summary's arbitrary
- * deterministic head at O(nd) memory) stores every final hidden state of
+ * state of the request's final token.  BUFFER (the Summary page's
+ * incremental-pooling paragraph: keep n x d values per request for a head
+ * that is not a streaming sum) stores every final hidden state of
  * the request at its position in the slot's buffer and, on the last chunk,
  * emits the mean of all N buffered rows, summed in an order fixed by N
  * alone; the buffer stays readable for any other head.  ORTHRUS_POOL_L2,

@@ -13,8 +13,10 @@ Readings: mean uses weight 1 per token; weighted mean uses the token's
 position 0 (first chunk); last keeps the row at position n-1 (the final
 chunk).
 
-The summary page adds that an arbitrary deterministic head can buffer all
-hidden states and run at the end at O(nd) memory.  Reading: the BUFFER
+Summary page, incremental-pooling paragraph: a head that is not a streaming
+sum can still be served, at a memory cost of n x d per request, by keeping
+every final hidden state until the last chunk and applying the head once
+there.  Reading: the BUFFER
 kind stores each chunk's final hidden states at their positions in the
 request (rows ctx_len .. ctx_len + n - 1 of the slot's buffer) and, on the
 last chunk, runs one head over all N buffered rows; the head computed here

@@ -95,7 +95,7 @@ def _run_chunks_buf(kind, H, chunks, dtype=np.float64, rows=None):
 
 
 def test_buffer_head_keeps_every_row_and_runs_the_mean_at_the_end():
-    # summary page: an arbitrary head buffers all hidden states (O(nd)) and runs at the end
+    # Summary page, incremental pooling: every row is kept (n x d) and the head runs once at the end
     H = RNG.standard_normal((300, 5))
     for chunks in ([300], [256, 44], [7] * 42 + [6], [1] * 300):
         e, pool = _run_chunks_buf(POOL_BUFFER, H, chunks, rows=320)
