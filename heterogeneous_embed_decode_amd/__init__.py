@@ -97,6 +97,8 @@ def _load():
     lib.orthrus_destroy.restype = None
     lib.orthrus_gemm_bf16.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.orthrus_gemm_bf16.restype = ctypes.c_int
+    lib.orthrus_lora_shrink_bf16.argtypes = [_vp, _i32, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp]
+    lib.orthrus_lora_shrink_bf16.restype = ctypes.c_int
     lib.orthrus_sample.argtypes = [_vp, ctypes.c_int64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
     lib.orthrus_sample.restype = ctypes.c_int
     lib.orthrus_fill_hash_bf16.argtypes = [_vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64, _vp]
@@ -127,7 +129,7 @@ EXPORTS = ("orthrus_pack", "orthrus_create", "orthrus_step", "orthrus_last_error
            "orthrus_destroy", "orthrus_gemm_bf16", "orthrus_profile", "orthrus_profile_read",
            "orthrus_fill_hash_bf16", "orthrus_sched_create", "orthrus_sched_submit",
            "orthrus_sched_next", "orthrus_sched_commit", "orthrus_sched_stats", "orthrus_sched_destroy",
-           "orthrus_sample", "orthrus_set_layer_dump", "orthrus_step_noalloc")
+           "orthrus_sample", "orthrus_set_layer_dump", "orthrus_step_noalloc", "orthrus_lora_shrink_bf16")
 
 
 class OrthrusError(RuntimeError):
@@ -232,6 +234,10 @@ def orthrus_destroy(eng) -> None:
 
 def orthrus_gemm_bf16(A, lda, B, ldb, C, ldc, M, N, K, epilogue, b_up_row=0, stream=None) -> int:
     return LIB.orthrus_gemm_bf16(A, lda, B, ldb, C, ldc, M, N, K, epilogue, b_up_row, stream)
+
+
+def orthrus_lora_shrink_bf16(X, ldx, A, rows, nr, K, scale, U, stream=None) -> int:
+    return LIB.orthrus_lora_shrink_bf16(X, ldx, A, rows, nr, K, scale, U, stream)
 
 
 def orthrus_set_layer_dump(eng, dst, cap_rows) -> int:

@@ -713,6 +713,18 @@ orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int3
   return r ? ORTHRUS_EHIP : ORTHRUS_OK;
 }
 
+orthrus_status orthrus_lora_shrink_bf16(const void *X, int32_t ldx, const void *A, int32_t rows, int32_t nr,
+                                        int32_t K, float scale, void *U, void *stream) {
+  if (rows < 0 || nr < 0 || K < 8 || K % 8 || ldx < K || ldx % 8) return ORTHRUS_EINVAL;
+  if (rows == 0 || nr == 0) return ORTHRUS_OK;
+  if (!X || !A || !U) return ORTHRUS_EINVAL;
+  if (!fits_buffer(((size_t)(rows - 1) * ldx + K) * 2) || !fits_buffer((size_t)nr * K * 2)) return ORTHRUS_EINVAL;
+  return launch_lora_shrink((const uint16_t *)X, ldx, (const uint16_t *)A, rows, nr, K, scale, (uint16_t *)U,
+                            stream)
+             ? ORTHRUS_EHIP
+             : ORTHRUS_OK;
+}
+
 orthrus_status orthrus_sample(const float *logits, int64_t ld, int32_t n_rows, int32_t vocab,
                               const float *temperature, const float *top_p, const uint32_t *uniforms,
                               int32_t *tokens, void *stream) {

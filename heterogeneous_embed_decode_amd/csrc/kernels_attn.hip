@@ -729,15 +729,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const DevItem *items,
       }
     }
     __syncthreads();
+    // the loads of up to eight partials are issued together, then their
+    // fmas run in partial order (np is uniform over the block)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int t = threadIdx.x + i * 256;
       if (t >= G * HD) break;
-      const int h = t / HD, d = t % HD;
-      float a = accs[i] * Ms[h];
-      const float *src = part_o + (size_t)(p0 + q0) * G * HD + h * HD + d;
-      for (int p = 0; p < np; ++p) a = fmaf(wts[h][p], src[(size_t)p * G * HD], a);
-      accs[i] = a;
+      const int h = t / HD;
+      float acc = accs[i] * Ms[h];
+      const float *src = part_o + (size_t)(p0 + q0) * G * HD + t;
+      for (int p = 0; p < np; p += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (p + u < np) v[u] = src[(size_t)(p + u) * G * HD];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (p + u < np) acc = fmaf(wts[h][p + u], v[u], acc);
+      }
+      accs[i] = acc;
     }
   }
   __syncthreads();

@@ -293,6 +293,25 @@ orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int3
                                  void *C, int32_t ldc, int32_t M, int32_t N, int32_t K,
                                  int32_t epilogue, int32_t b_up_row, void *stream);
 
+/* Adapter shrink U = bf16(scale * X A^T): the first half of the low-rank
+ * update that embedding rows take in the QKV and O projections (full text
+ * §2.2 Parameter sharing: the embedding task shares the backbone and adds
+ * a LoRA adapter; §5.1 places it on q, k, v and o).  The step runs the
+ * same code; this entry point exists for tests and timing.
+ *  X      device bf16 [rows][ldx], ldx >= K (the normed rows, or the
+ *         attention output for the O adapter)
+ *  A      device bf16 [nr][K]: the adapter's down-projection, one row per
+ *         output column (nr = 3 x rank for QKV, rank for O)
+ *  U      device bf16 [rows][nr] out
+ * Runs the projection GEMM kernel with `scale` folded into its bf16
+ * epilogue (a whole tile's K sum per workgroup, so the result does not
+ * depend on timing).  Asynchronous on
+ * `stream`; allocates nothing.  EINVAL for rows or nr < 0, K < 8, K % 8,
+ * ldx < K, ldx % 8, NULL pointers with rows, nr > 0, or operands spanning
+ * 2 GiB or more; EHIP on launch failure. */
+orthrus_status orthrus_lora_shrink_bf16(const void *X, int32_t ldx, const void *A, int32_t rows,
+                                        int32_t nr, int32_t K, float scale, void *U, void *stream);
+
 /* Next-token choice for logit rows (full text §3.1: the emit stage hands
  * every generation request's last-row logits to the sampler; §2.2
  * Generation: one new token per decoding step).  One workgroup per row.

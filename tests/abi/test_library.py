@@ -159,3 +159,19 @@ def test_create_rejects_unknown_dtype_before_device_work():
         with pytest.raises(hed.OrthrusError) as e:
             hed.orthrus_create(cfg, 8, 8, 8, layers, 8, 8)
         assert e.value.code == want
+
+
+def test_lora_shrink_rejects_bad_sizes_before_device_work():
+    """orthrus_lora_shrink_bf16's argument checks run before any HIP call
+    (the dummy pointers are never dereferenced)."""
+    p = 256
+    assert hed.orthrus_lora_shrink_bf16(p, 32, p, 1, 1, 4, 1.0, p) == hed.EINVAL        # K < 8
+    assert hed.orthrus_lora_shrink_bf16(p, 32, p, 1, 1, 40, 1.0, p) == hed.EINVAL       # ldx < K
+    assert hed.orthrus_lora_shrink_bf16(p, 36, p, 1, 1, 36, 1.0, p) == hed.EINVAL       # K % 8
+    assert hed.orthrus_lora_shrink_bf16(p, 44, p, 1, 1, 40, 1.0, p) == hed.EINVAL       # ldx % 8
+    assert hed.orthrus_lora_shrink_bf16(p, 32, p, -1, 1, 32, 1.0, p) == hed.EINVAL      # rows < 0
+    assert hed.orthrus_lora_shrink_bf16(p, 32, p, 1, -2, 32, 1.0, p) == hed.EINVAL      # nr < 0
+    assert hed.orthrus_lora_shrink_bf16(None, 32, p, 1, 1, 32, 1.0, p) == hed.EINVAL    # NULL X
+    assert hed.orthrus_lora_shrink_bf16(p, 32, p, 1, 1, 32, 1.0, None) == hed.EINVAL    # NULL U
+    assert hed.orthrus_lora_shrink_bf16(p, 1 << 20, p, 1 << 11, 1, 1024, 1.0, p) == hed.EINVAL  # X spans 4 GiB
+    assert hed.orthrus_lora_shrink_bf16(None, 32, None, 0, 1, 32, 1.0, None) == hed.OK  # nothing to do

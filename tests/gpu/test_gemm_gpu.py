@@ -89,3 +89,32 @@ def test_gemm_swiglu(M, F, K):
 def test_gemm_rejects_bad_sizes():
     assert hed.orthrus_gemm_bf16(1, 12, 1, 12, 1, 4, 4, 4, 12, 0) == hed.EINVAL
     assert hed.orthrus_gemm_bf16(1, 16, 1, 16, 1, 4, 4, 4, 16, 9) == hed.EINVAL
+
+
+# Adapter shrink U = bf16(s X A^T) through its own entry point: ragged row
+# and column tiles, a row stride wider than K, and scales other than 1 (the
+# scale is folded into the GEMM's bf16 epilogue).
+SHRINK = [(1, 16, 32, 1.0, 0), (15, 48, 64, 0.5, 0), (17, 24, 96, 2.0, 8), (300, 64, 4096, 1.0, 0),
+          (7168, 48, 4096, 1.0, 0), (4096, 16, 4096, 0.25, 0), (129, 1, 160, 1.0, 0), (33, 40, 224, 3.0, 16),
+          (200, 80, 256, 1.0, 0), (50, 16, 72, 1.0, 0)]
+
+
+@pytest.mark.parametrize("rows,nr,K,scale,pad", SHRINK)
+def test_lora_shrink(rows, nr, K, scale, pad):
+    print(f"shrink rows={rows} nr={nr} K={K} scale={scale} pad={pad}", flush=True)
+    rng = np.random.default_rng(rows * 31 + nr * 7 + K)
+    ldx = K + pad
+    x_bits, X = _bf16(rng, (rows, ldx))
+    a_bits, A = _bf16(rng, (nr, K), 0.02)
+    ref = scale * (X[:, :K] @ A.T)
+    U = torch.zeros((rows, nr), dtype=torch.int16, device="cuda")
+    dX, dA = _dev(x_bits), _dev(a_bits)  # held until the kernel has run
+    st = hed.orthrus_lora_shrink_bf16(dX.data_ptr(), ldx, dA.data_ptr(), rows, nr, K, scale, U.data_ptr())
+    assert st == hed.OK
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f32(U.cpu().numpy().view(np.uint16)).astype(np.float64)
+    # one bf16 rounding of an fp32 sum: 2^-8 relative per element plus the
+    # fp32 accumulation error, far below it at these K
+    err = np.abs(got - ref)
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.sqrt(K)), (float(err.max()), rows, nr, K)
+
