@@ -122,20 +122,30 @@ def host_description():
     return {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas": blas}
 
 
-def decode_only(batch):
-    """The decode items of a batch as a batch of their own (page lists
-    re-based), for timing decode attention alone."""
+def sub_batch(batch, keep):
+    """The items of a batch that `keep` selects, as a batch of their own
+    (page lists re-based), for timing one side of the ragged attention."""
     from synth import workloads as wl
     items, toks, pages = [], [], []
     t = 0
     for i, it in enumerate(batch.items):
-        if it.kind == wl.DECODE:
+        if keep(it):
             items.append(wl.Item(**{**it.__dict__, "page_off": len(pages)}))
             pages.extend(batch.item_pages(i).tolist())
-            toks.append(int(batch.token_ids[t]))
+            toks.extend(int(x) for x in batch.token_ids[t:t + it.n_tokens])
         t += it.n_tokens
     import numpy as np
     return wl.Batch(items, np.asarray(toks, np.int32), np.asarray(pages, np.int32))
+
+
+def decode_only(batch):
+    from synth import workloads as wl
+    return sub_batch(batch, lambda it: it.kind == wl.DECODE)
+
+
+def chunk_only(batch):
+    from synth import workloads as wl
+    return sub_batch(batch, lambda it: it.kind != wl.DECODE)
 
 
 def pool_bytes(cfg, batch):
@@ -316,6 +326,8 @@ def main():
                          "(temperature 0.8, top-p 0.9); prints the sampler object")
     ap.add_argument("--decode-only", action="store_true",
                     help="with --counters: run only the decode items of each step (decode attention alone)")
+    ap.add_argument("--chunk-only", action="store_true",
+                    help="with --counters: run only the embedding and prefill items of each step")
     ap.add_argument("--counters", action="store_true",
                     help="run only --warmup + --steps steps of the workload and exit (for rocprofv3 counter "
                          "passes; no JSON line)")
@@ -407,8 +419,8 @@ def main():
             rows_done[0] += batches[j].n_tokens
 
     if args.counters:
-        if args.decode_only:
-            batches[:] = [decode_only(b) for b in batches]
+        if args.decode_only or args.chunk_only:
+            batches[:] = [(decode_only if args.decode_only else chunk_only)(b) for b in batches]
             bargs[:] = [dev.step_args(b) for b in batches]
         run(args.warmup + args.steps)
         torch.cuda.synchronize()
@@ -498,29 +510,40 @@ def main():
         r_avg = prof["attn_ragged"]["total_ms"] / prof["attn_ragged"]["count"] * 1e-3
         t_r = work["attn_chunk"][0] / (PEAK_BF16_TFLOPS * 1e12) + work["attn_decode"][1] / (PEAK_HBM_GBS * 1e9)
         roof["attn_ragged_frac"] = round(t_r / r_avg, 4)
-    # decode attention is the HBM-bound part of the path: its bandwidth, timed
-    # on the same steps' decode rows alone
-    dec_batches = [decode_only(b) for b in batches]
-    if any(b.n_items for b in dec_batches):
-        dargs = [dev.step_args(b) for b in dec_batches]
-        for j, b in enumerate(dec_batches):
-            s_, _, _ = dev.step(b, stream=sptr, args=dargs[j])
+    # the two sides of the ragged attention, each timed on the same steps'
+    # rows alone: decode rows (HBM-bound: K/V bytes over 8 TB/s) and chunk
+    # rows (matrix-bound: causal-pair flops over 2.5 PFLOP/s)
+    def attn_alone(subs):
+        sargs = [dev.step_args(b) for b in subs]
+        for j, b in enumerate(subs):
+            s_, _, _ = dev.step(b, stream=sptr, args=sargs[j])
             assert s_ == hed.OK
         torch.cuda.synchronize()
         hed.orthrus_profile(dev.eng, True)
-        for _ in range(max(1, args.steps // len(dec_batches))):
-            for j, b in enumerate(dec_batches):
-                s_, _, _ = dev.step(b, stream=sptr, args=dargs[j])
+        for _ in range(max(1, args.steps // len(subs))):
+            for j, b in enumerate(subs):
+                s_, _, _ = dev.step(b, stream=sptr, args=sargs[j])
                 assert s_ == hed.OK
         torch.cuda.synchronize()
-        dprof = hed.orthrus_profile_read(dev.eng)
+        sprof = hed.orthrus_profile_read(dev.eng)
         hed.orthrus_profile(dev.eng, False)
-        d_avg = dprof["attn_ragged"]["total_ms"] / dprof["attn_ragged"]["count"] * 1e-3
+        return sprof["attn_ragged"]["total_ms"] / sprof["attn_ragged"]["count"] * 1e-3
+
+    dec_batches = [decode_only(b) for b in batches]
+    if any(b.n_items for b in dec_batches):
+        d_avg = attn_alone(dec_batches)
         d_bytes = sum(kernel_work(cfg, b, m)["attn_decode"][1] for b, m in zip(batches, metas)) / len(batches)
         roof["attn_decode_hbm_gbs"] = round(d_bytes / d_avg / 1e9, 1)
         roof["attn_decode_hbm_frac"] = round(d_bytes / d_avg / 1e9 / PEAK_HBM_GBS, 4)
         roof["attn_decode_avg_ms"] = round(d_avg * 1e3, 5)
         roof["attn_decode_traffic"] = traffic_from_profiles("attn_ragged_decode", args.workload)
+    chk_batches = [chunk_only(b) for b in batches]
+    if any(b.n_items for b in chk_batches):
+        c_avg = attn_alone(chk_batches)
+        c_flops = sum(kernel_work(cfg, b, m)["attn_chunk"][0] for b, m in zip(batches, metas)) / len(batches)
+        roof["attn_chunk_tflops"] = round(c_flops / c_avg / 1e12, 1)
+        roof["attn_chunk_mfma_frac"] = round(c_flops / c_avg / 1e12 / PEAK_BF16_TFLOPS, 4)
+        roof["attn_chunk_avg_ms"] = round(c_avg * 1e3, 5)
 
     sampler = measure_sampler(dev, cfg, meta, stream, run)
     cpu = None

@@ -59,6 +59,7 @@ __device__ __forceinline__ int slot_of(const AttnArgs &a, int key) {
 }
 
 constexpr int CKT = 64;  // keys per chunk-path tile
+constexpr float CHUNK_RESCALE_LOG2 = 8.f;  // lazy-rescale threshold of the chunk path (log2 units)
 
 // Chunk-path LDS: two buffers of one 64-key tile of K and of V, both in
 // the cache's [key][head dim] order with 16-byte chunks swizzled per key.
@@ -90,7 +91,9 @@ __device__ __forceinline__ int vswz(int key) { return VCH >= 8 ? 2 * (key & 3) :
 // t is consumed from LDS; one barrier per tile publishes the next buffer.
 //  S^T = K Q^T    : 32x32x16 MFMAs, K rows from LDS (ds_read_b128), Q^T in
 //                   registers for the whole item.
-//  softmax        : online, fp32, exp2 domain, per query row (lane column).
+//  softmax        : online, fp32, exp2 domain, per query row (lane column),
+//                   rescaled lazily (only when a row's max grows by more
+//                   than 8 in log2 units).
 //  O^T += V^T P^T : P^T is the S^T accumulator packed to bf16 (its key
 //                   order within a 16-key step is 4h..4h+3, 8+4h..8+4h+3 for
 //                   lane half h); the V^T operand takes exactly those keys
@@ -204,10 +207,11 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[kk], s[kb], 0, 0, 0);
       }
     }
-    // scale, causal mask (only tiles that reach past the first row's
-    // position need it; it also hides the clamped keys past the item),
-    // tile max.  Query rows past the chunk compute on zero q and are
-    // never written.
+    // causal mask (only tiles that reach past the first row's position
+    // need it; it also hides the clamped keys past the item) and the tile
+    // max of the raw scores; the scale (> 0) is applied to the max and
+    // folded into the exponent below.  Query rows past the chunk compute on
+    // zero q and are never written.
     float mt = -INFINITY;
     if (kt0 + CKT - 1 > min_rpos) {
 #pragma unroll
@@ -215,7 +219,7 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kt0 + kb * 32 + (e / 4) * 8 + half * 4 + (e % 4);
-          const float v = key > rpos ? -INFINITY : s[kb][e] * a.scale_log2;
+          const float v = key > rpos ? -INFINITY : s[kb][e];
           s[kb][e] = v;
           mt = fmaxf(mt, v);
         }
@@ -223,30 +227,36 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
 #pragma unroll
       for (int kb = 0; kb < CKT / 32; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          s[kb][e] *= a.scale_log2;
-          mt = fmaxf(mt, s[kb][e]);
-        }
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.scale_log2;
+    // lazy rescaling: the running max (and with it l and the output
+    // accumulators) moves only when some row of the wave meets a tile max
+    // above it by more than CHUNK_RESCALE_LOG2; otherwise the stale max
+    // stays and p = 2^(s c - m) stays below 2^CHUNK_RESCALE_LOG2, which bf16
+    // P and the fp32 sums hold without loss.  The first tile always moves
+    // it (every row sees key 0).
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + CHUNK_RESCALE_LOG2) != 0) {  // uniform over the wave
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < CKT / 32; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pr = __builtin_amdgcn_exp2f(s[kb][e] - m_use);
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][e], a.scale_log2, -m_use));
         s[kb][e] = pr;
         lsum += pr;
       }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int i = 0; i < NDB; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+    l_run += lsum;
 
     // O^T += V^T P^T in 16-key steps
     const int g = lane >> 4, jj = lane & 15;
