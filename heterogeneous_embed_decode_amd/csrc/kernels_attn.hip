@@ -70,9 +70,17 @@ struct ChunkSmem {
   uint16_t K[2][CKT * HD];
   uint16_t V[2][CKT * VD];
 };
+// every buffer starts on a 256-byte boundary of a 256-byte aligned struct
+static_assert((CKT * 16 * 2) % 256 == 0, "K and V buffers of every head dim are 256-byte multiples");
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+
+// 32-bit LDS address of a shared-memory object
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
 
 // LDS stores of this thread have landed, then the workgroup barrier; no
 // wait on global loads in flight (which __syncthreads' fence would add),
@@ -137,37 +145,88 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
     }
   }
 
-  // this thread's chunks of a tile: chunk i = tid + 256 j is key i / NCH,
-  // head-dim chunk i % NCH (keys past the item re-read its last key)
+  // this thread's chunks of a tile: chunk i = tid + 256 j is key
+  // kj0 + KJS j (kj0 = tid / NCH, KJS = 256 / NCH), head-dim chunk
+  // cj = tid % NCH; keys past the item re-read its last key.  KJS is a
+  // multiple of NCH and of 4 (HD <= 128), so the K swizzle (key mod NCH) and
+  // the V swizzle (key mod 4) are the same for every j: a chunk's LDS slot
+  // is one per-thread base plus j KJS rows.
+  constexpr int KJS = 256 / NCH;
+  static_assert(KJS % NCH == 0 && KJS % 4 == 0, "swizzle is per thread");
+  const int kj0 = tid / NCH, cj = tid % NCH;
   u32x4_t kreg[NLD], vreg[NLD];
   int pg[NLD];
   auto chunk_ok = [&](int j) { return NLD * 256 == CKT * NCH || tid + 256 * j < CKT * NCH; };
+  // Power-of-two pages of at most 64 keys split every whole tile evenly:
+  // chunk j of tile t then sits in page t * ppt + (its key in the tile) /
+  // ps at a fixed slot, so its offset is page id x page stride plus a
+  // per-thread constant.  Other page sizes, and the last tile (clamped
+  // keys), take the general per-key form.
+  const bool fast = a.ps_log2 >= 0 && a.ps <= CKT;
+  const int ppt = fast ? CKT >> a.ps_log2 : 0;
+  const uint32_t pstride = (uint32_t)a.Hkv * a.ps * HD;  // elements per page of one layer
+  auto whole = [&](int t) { return fast && (t + 1) * CKT <= nkeys; };
   auto lookup = [&](int t) {
+    if (whole(t)) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j)
-      if (chunk_ok(j)) pg[j] = pages[page_of(a, min(t * CKT + (tid + 256 * j) / NCH, nkeys - 1))];
+      for (int j = 0; j < NLD; ++j)
+        if (chunk_ok(j)) pg[j] = pages[t * ppt + ((kj0 + KJS * j) >> a.ps_log2)];
+    } else {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        if (chunk_ok(j)) pg[j] = pages[page_of(a, min(t * CKT + kj0 + KJS * j, nkeys - 1))];
+    }
   };
   auto load = [&](int t) {
+    if (whole(t)) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      if (!chunk_ok(j)) continue;
-      const int i = tid + 256 * j;
-      const int p = min(t * CKT + i / NCH, nkeys - 1);
-      const size_t off = (((size_t)pg[j] * a.Hkv + w.kvh) * a.ps + slot_of(a, p)) * HD + (i % NCH) * 8;
-      kreg[j] = *(const u32x4_t *)(a.kc + off);
-      vreg[j] = *(const u32x4_t *)(a.vc + off);
+      for (int j = 0; j < NLD; ++j) {
+        if (!chunk_ok(j)) continue;
+        const int slot = (kj0 + KJS * j) & (a.ps - 1);
+        const size_t off = (size_t)(uint32_t)pg[j] * pstride + (uint32_t)((w.kvh * a.ps + slot) * HD + cj * 8);
+        kreg[j] = *(const u32x4_t *)(a.kc + off);
+        vreg[j] = *(const u32x4_t *)(a.vc + off);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        if (!chunk_ok(j)) continue;
+        const int p = min(t * CKT + kj0 + KJS * j, nkeys - 1);
+        const size_t off = (((size_t)pg[j] * a.Hkv + w.kvh) * a.ps + slot_of(a, p)) * HD + cj * 8;
+        kreg[j] = *(const u32x4_t *)(a.kc + off);
+        vreg[j] = *(const u32x4_t *)(a.vc + off);
+      }
     }
   };
+  // LDS byte addresses: the buffers start on 256-byte boundaries, so the
+  // XOR terms below (bits 4..7 of a row) never meet the row, block or
+  // buffer bits and can be applied after adding those
+  const uint32_t k_lds = lds_addr(&sm.K[0][0]), v_lds = lds_addr(&sm.V[0][0]);
+  const uint32_t st_k = 2u * (kj0 * HD + ((cj ^ (kj0 & (NCH - 1))) * 8));
+  const uint32_t st_v = 2u * (kj0 * VD + ((cj ^ vswz<VCH>(kj0)) * 8));
   auto store = [&](int b) {
+    const uint32_t kb_ = k_lds + b * (CKT * HD * 2) + st_k, vb_ = v_lds + b * (CKT * VD * 2) + st_v;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       if (!chunk_ok(j)) continue;
-      const int i = tid + 256 * j;
-      const int key = i / NCH, c = i % NCH;
-      *(u32x4_t *)(&sm.K[b][key * HD + ((c ^ (key & (NCH - 1))) * 8)]) = kreg[j];
-      *(u32x4_t *)(&sm.V[b][key * VD + ((c ^ vswz<VCH>(key)) * 8)]) = vreg[j];
+      *(lds_u32x4_t *)(kb_ + j * (KJS * HD * 2)) = kreg[j];
+      *(lds_u32x4_t *)(vb_ + j * (KJS * VD * 2)) = vreg[j];
     }
   };
+  // K operand of key row (lane & 31) of a 32-key block, head-dim chunk
+  // 2 kk + half, swizzled by x = lane mod NCH: with x' = x / 2 its element
+  // index is (row HD + 16 x' + 8 (half ^ (x & 1))) XOR 16 kk
+  const int xk = lane & (NCH - 1);
+  const uint32_t k_rd = 2u * ((lane & 31) * HD + 16 * (xk >> 1) + 8 * (half ^ (xk & 1)));
+  // V^T operand (ds_read_b64_tr_b16): key 4 half + jj / 4 of an 8-key
+  // group, dims 32 db + 16 (g & 1) + 4 (jj & 3) ..; the row swizzle
+  // c = 2 (jj / 4 mod 4) (rows of 8 or more chunks) turns the index into
+  // (key VD + 32 (c / 4) + 8 (u ^ (c & 3)) + 4 (jj & 1)) XOR 32 db with
+  // u = 2 (g & 1) + (jj & 3) / 2
+  const int g = lane >> 4, jj = lane & 15;
+  const int vc_ = VCH >= 8 ? 2 * ((jj >> 2) & 3) : 0;
+  const int vu = 2 * (g & 1) + ((jj & 3) >> 1);
+  const uint32_t v_rd = 2u * ((4 * half + (jj >> 2)) * VD + 32 * (vc_ >> 2) + 8 * (vu ^ (vc_ & 3)) + 4 * (jj & 1));
 
   f32x16_t oacc[NDB];
 #pragma unroll
@@ -189,8 +248,8 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
     }
     lds_barrier();
     const int kt0 = t * CKT;
-    const uint16_t *Kt = sm.K[b];
-    const uint16_t *Vt = sm.V[b];
+    const uint32_t kt = k_lds + b * (CKT * HD * 2) + k_rd;
+    const uint32_t vt = v_lds + b * (CKT * VD * 2) + v_rd;
 
     // S^T for the tile's two 32-key blocks
     f32x16_t s[CKT / 32];
@@ -198,12 +257,10 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
     for (int kb = 0; kb < CKT / 32; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-      const int key = kb * 32 + (lane & 31);
 #pragma unroll
       for (int kk = 0; kk < HD / 16; ++kk) {
-        const int ch = kk * 2 + half;
         const bf16x8_t kop =
-            __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(&Kt[key * HD + ((ch ^ (key & (NCH - 1))) * 8)]));
+            __builtin_bit_cast(bf16x8_t, *(const lds_u32x4_t *)((kt ^ (32u * kk)) + kb * (32 * HD * 2)));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[kk], s[kb], 0, 0, 0);
       }
     }
@@ -259,7 +316,6 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
     l_run += lsum;
 
     // O^T += V^T P^T in 16-key steps
-    const int g = lane >> 4, jj = lane & 15;
 #pragma unroll
     for (int st = 0; st < CKT / 16; ++st) {
       const int kb = st / 2, e0 = (st % 2) * 8;
@@ -268,13 +324,11 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
       for (int i = 0; i < 8; ++i) pop[i] = (__bf16)s[kb][e0 + i];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int dim = db * 32 + (g & 1) * 16 + 4 * (jj & 3);
         u32x2_t vv[2];
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
-          const int key = st * 16 + rr * 8 + 4 * half + (jj >> 2);
-          const uint16_t *src = &Vt[key * VD + (((dim >> 3) ^ vswz<VCH>(key)) * 8) + (dim & 7)];
-          const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(src));
+          const uint32_t src = (vt ^ (64u * db)) + (st * 16 + rr * 8) * (VD * 2);
+          const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)src);
           vv[rr] = __builtin_bit_cast(u32x2_t, v);
         }
         u32x4_t vw;
@@ -677,7 +731,8 @@ union RaggedSmem {
 
 template <int HD, int G>
 __global__ __launch_bounds__(256, 2) void attn_ragged_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) RaggedSmem<HD, G> sm;
+  // 256-byte alignment: the chunk path's address XORs rely on it
+  __shared__ __attribute__((aligned(256))) RaggedSmem<HD, G> sm;
   const AttnWork w = a.work[blockIdx.x];
   if (w.type == WORK_CHUNK) {
     chunk_path<HD>(a, w, sm.c);
