@@ -447,17 +447,23 @@ def main():
     print(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, {ev_ms / args.steps:.3f} ms/step events",
           file=sys.stderr, flush=True)
 
-    # per distinct step: HIP events around each step on its stream
+    # per distinct step: HIP events around R repeats of the step on its
+    # stream, after one untimed repeat, so the host enqueues ahead of the
+    # device (a step timed alone between two events would include the host's
+    # launch time while the device idles)
     per_step = []
+    reps = max(2, args.steps // len(batches))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in batches]
     for j, b in enumerate(batches):
-        ev[j][0].record(stream)
-        s_, _, _ = dev.step(b, stream=sptr, args=bargs[j])
-        assert s_ == hed.OK
+        for r in range(reps + 1):
+            if r == 1:
+                ev[j][0].record(stream)
+            s_, _, _ = dev.step(b, stream=sptr, args=bargs[j])
+            assert s_ == hed.OK
         ev[j][1].record(stream)
     torch.cuda.synchronize()
     for j, b in enumerate(batches):
-        ms = ev[j][0].elapsed_time(ev[j][1])
+        ms = ev[j][0].elapsed_time(ev[j][1]) / reps
         roof_ms, _ = step_roofline_ms(cfg, b, metas[j])
         per_step.append({"step": j, "rows": b.n_tokens, "embed_rows": int(metas[j]["n_embed_rows"]),
                          "decode_rows": int(metas[j]["n_decode_rows"]), "ms": round(ms, 3),

@@ -87,11 +87,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // and a compiler barrier for LDS accesses
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// 16-byte chunk swizzle of a V row: ds_read_b64_tr_b16 lets 16 lanes read
-// 4 consecutive keys x 32 bytes; XOR with 2 (key & 3) puts those 4 rows on
-// distinct banks.  Rows of fewer than 8 chunks are not swizzled.
+// 16-byte chunk swizzle of a V row.  One 32-lane cycle of
+// ds_read_b64_tr_b16 reads 4 consecutive keys x 2 groups of 16 dims (4
+// chunks per key); XOR with 4 (key & 3) (rows of 16 chunks, all starting on
+// bank 0) or 4 ((key >> 1) & 1) (rows of 8 chunks, odd rows on bank 32)
+// gives those 16 chunks 16 distinct 4-bank groups.  Rows of 4 chunks
+// already start on 4 different bank quarters.
 template <int VCH>
-__device__ __forceinline__ int vswz(int key) { return VCH >= 8 ? 2 * (key & 3) : 0; }
+__device__ __forceinline__ int vswz(int key) {
+  return VCH >= 16 ? 4 * (key & 3) : VCH == 8 ? 4 * ((key >> 1) & 1) : 0;
+}
 
 // Chunk work: 128 (token, head) rows of one item and KV head (32 query
 // rows per wave), keys in 64-key tiles.  The K and V chunks of tile t+1 are
@@ -106,7 +111,8 @@ __device__ __forceinline__ int vswz(int key) { return VCH >= 8 ? 2 * (key & 3) :
 //                   order within a 16-key step is 4h..4h+3, 8+4h..8+4h+3 for
 //                   lane half h); the V^T operand takes exactly those keys
 //                   with two ds_read_b64_tr_b16, whose 16-lane groups turn
-//                   4 keys x 4 dims per lane into 4 keys of one dim per lane.
+//                   4 keys x 4 dims per lane into 4 keys of one dim per lane
+//                   (V rows swizzled so that those reads meet no bank twice).
 template <int HD>
 __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &sm) {
   constexpr int NCH = HD / 8;                       // 16-byte chunks per K row
@@ -219,14 +225,13 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
   const int xk = lane & (NCH - 1);
   const uint32_t k_rd = 2u * ((lane & 31) * HD + 16 * (xk >> 1) + 8 * (half ^ (xk & 1)));
   // V^T operand (ds_read_b64_tr_b16): key 4 half + jj / 4 of an 8-key
-  // group, dims 32 db + 16 (g & 1) + 4 (jj & 3) ..; the row swizzle
-  // c = 2 (jj / 4 mod 4) (rows of 8 or more chunks) turns the index into
-  // (key VD + 32 (c / 4) + 8 (u ^ (c & 3)) + 4 (jj & 1)) XOR 32 db with
-  // u = 2 (g & 1) + (jj & 3) / 2
+  // group, dims 32 db + 16 (g & 1) + 4 (jj & 3) ..; the row swizzle c (a
+  // multiple of 4 chunks) turns the index into
+  // (key VD + 32 (c / 4) + 8 u + 4 (jj & 1)) XOR 32 db, u = 2 (g & 1) + (jj & 3) / 2
   const int g = lane >> 4, jj = lane & 15;
-  const int vc_ = VCH >= 8 ? 2 * ((jj >> 2) & 3) : 0;
+  const int vkey = 4 * half + (jj >> 2);
   const int vu = 2 * (g & 1) + ((jj & 3) >> 1);
-  const uint32_t v_rd = 2u * ((4 * half + (jj >> 2)) * VD + 32 * (vc_ >> 2) + 8 * (vu ^ (vc_ & 3)) + 4 * (jj & 1));
+  const uint32_t v_rd = 2u * (vkey * VD + 32 * (vswz<VCH>(vkey) >> 2) + 8 * vu + 4 * (jj & 1));
 
   f32x16_t oacc[NDB];
 #pragma unroll
