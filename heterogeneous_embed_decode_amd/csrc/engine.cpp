@@ -137,7 +137,7 @@ void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const
       for (int g = 0; g < cfg.n_kv_heads; ++g)
         for (int q0 = 0; q0 < it.n_tokens; q0 += QB) {
           const int qn = std::min(QB, it.n_tokens - q0);
-          work.push_back({WORK_CHUNK, i, g, q0, qn, 0, it.ctx_len + q0 + qn, 0});
+          work.push_back({WORK_CHUNK, i, g, q0, qn, 0, it.ctx_len + q0 + qn, 0, d.row0, d.ctx, d.page_off, 0});
         }
     } else {
       const int nk = it.ctx_len + 1;
@@ -147,7 +147,8 @@ void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const
       for (int g = 0; g < cfg.n_kv_heads; ++g)
         for (int s = 0; s < ns; ++s) {
           const int k0 = s * split;
-          dec.push_back({WORK_DECODE, i, g, 0, 1, k0, std::min(nk, k0 + split), n_parts + g * ns + s});
+          dec.push_back({WORK_DECODE, i, g, 0, 1, k0, std::min(nk, k0 + split), n_parts + g * ns + s, d.row0, d.ctx,
+                         d.page_off, 0});
         }
       n_parts += cfg.n_kv_heads * ns;
     }
@@ -390,7 +391,7 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
   const size_t o_segs = off; off = align4(off + n_segs * 8);
   const size_t o_dec = off; off = align4(off + dec_items.size());
   const size_t o_items = off; off = align4(off + eng->items.size() * 8);
-  const size_t o_work = off; off = align4(off + eng->work.size() * 8);
+  const size_t o_work = off; off = align4(off + eng->work.size() * (sizeof(AttnWork) / 4));
   const size_t o_norm = off; off = align4(off + norm_rows.size());
   const size_t o_ritem = off; off = align4(off + (c.dtype == ORTHRUS_F32 ? (size_t)T : 0));
   const size_t words = std::max<size_t>(off, 4);
@@ -468,7 +469,7 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
   if (n_segs) memcpy(mh + o_segs, p.pool_segs.data(), n_segs * 8 * 4);
   if (!dec_items.empty()) memcpy(mh + o_dec, dec_items.data(), dec_items.size() * 4);
   if (!eng->items.empty()) memcpy(mh + o_items, eng->items.data(), eng->items.size() * 32);
-  if (!eng->work.empty()) memcpy(mh + o_work, eng->work.data(), eng->work.size() * 32);
+  if (!eng->work.empty()) memcpy(mh + o_work, eng->work.data(), eng->work.size() * sizeof(AttnWork));
   if (!norm_rows.empty()) memcpy(mh + o_norm, norm_rows.data(), norm_rows.size() * 4);
   if (c.dtype == ORTHRUS_F32) memcpy(mh + o_ritem, p.row_item.data(), (size_t)T * 4);
   if (eng->done_pending && eng->last_stream != s)

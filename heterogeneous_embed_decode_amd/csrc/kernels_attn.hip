@@ -121,21 +121,20 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
   constexpr int NDB = VD / 32;                      // 32-dim blocks of O^T
   constexpr int NLD = (CKT * NCH + 255) / 256;      // chunks per thread per tile (each of K and V)
   const int G = a.Hq / a.Hkv;
-  const DevItem it = a.items[w.item];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5;
   const int r = wave * 32 + (lane & 31);
   const int tok = w.q0 + r / G;
   const int head = w.kvh * G + r % G;
   const bool rvalid = (r / G) < w.qn;
-  const int rpos = it.ctx + tok;
-  const int nkeys = it.ctx + w.q0 + w.qn;
+  const int rpos = w.ctx + tok;
+  const int nkeys = w.ctx + w.q0 + w.qn;
   const int ntiles = (nkeys + CKT - 1) / CKT;
-  const int32_t *pages = a.page_ids + it.page_off;
+  const int32_t *pages = a.page_ids + w.page_off;
 
   bf16x8_t q[HD / 16];
   {
-    const uint16_t *qrow = a.qkv + (size_t)(it.row0 + (rvalid ? tok : 0)) * a.ld_qkv + head * HD;
+    const uint16_t *qrow = a.qkv + (size_t)(w.row0 + (rvalid ? tok : 0)) * a.ld_qkv + head * HD;
 #pragma unroll
     for (int kk = 0; kk < HD / 16; ++kk) {
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -239,7 +238,7 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const int min_rpos = it.ctx + w.q0;
+  const int min_rpos = w.ctx + w.q0;
 
   lookup(0);
   load(0);
@@ -345,7 +344,7 @@ __device__ void chunk_path(const AttnArgs &a, const AttnWork &w, ChunkSmem<HD> &
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!rvalid) return;
   const float inv = 1.f / l_tot;
-  uint16_t *orow = a.o + (size_t)(it.row0 + tok) * a.ld_o + head * HD;
+  uint16_t *orow = a.o + (size_t)(w.row0 + tok) * a.ld_o + head * HD;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -396,9 +395,9 @@ __device__ __forceinline__ float dot2(uint32_t q2, uint32_t k2, float c) {
 // decode split and write either the finished output row (the split covers
 // the whole context) or the split's partial for the combine kernel.
 template <int HD, int G>
-__device__ void finish_decode(const AttnArgs &a, const AttnWork &w, const DevItem &it,
+__device__ void finish_decode(const AttnArgs &a, const AttnWork &w,
                               const float (*o)[G * HD], const float (*ml)[G][2]) {
-  const bool whole = (w.k0 == 0 && w.k1 == it.ctx + 1);
+  const bool whole = (w.k0 == 0 && w.k1 == w.ctx + 1);
   for (int t = threadIdx.x; t < G * HD; t += 256) {
     const int h = t / HD, d = t % HD;
     float M = -INFINITY;
@@ -413,7 +412,7 @@ __device__ void finish_decode(const AttnArgs &a, const AttnWork &w, const DevIte
       O += wgt * o[v][t];
     }
     if (whole) {
-      a.o[(size_t)it.row0 * a.ld_o + (w.kvh * G + h) * HD + d] = (uint16_t)f2bf(O / L);
+      a.o[(size_t)w.row0 * a.ld_o + (w.kvh * G + h) * HD + d] = (uint16_t)f2bf(O / L);
     } else {
       a.part_o[((size_t)w.part * G + h) * HD + d] = O;
       if (d == 0) {
@@ -438,12 +437,11 @@ __device__ void decode_path(const AttnArgs &a, const AttnWork &w, DecodeSmem<HD,
   constexpr int WK = DEC_SPLIT_VEC / ATTN_WAVES;  // keys per wave
   constexpr int NL = WK / KPI > 0 ? WK / KPI : 1;
   static_assert(NL * KPI >= WK, "wave key span");
-  const DevItem it = a.items[w.item];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPK, kg = lane / LPK;
   const int pi0 = page_of(a, w.k0);
   const int npg = page_of(a, w.k1 - 1) - pi0 + 1;
-  for (int t = threadIdx.x; t < npg; t += 256) sm.pages[t] = a.page_ids[it.page_off + pi0 + t];
+  for (int t = threadIdx.x; t < npg; t += 256) sm.pages[t] = a.page_ids[w.page_off + pi0 + t];
   __syncthreads();
   const int wk0 = w.k0 + wave * WK;
   const int wk1 = min(w.k1, wk0 + WK);
@@ -468,7 +466,7 @@ __device__ void decode_path(const AttnArgs &a, const AttnWork &w, DecodeSmem<HD,
       vr[li] = *(const u32x4_t *)(a.vc + off);
     }
     u32x4_t q[G];
-    const uint16_t *qrow = a.qkv + (size_t)it.row0 * a.ld_qkv + (w.kvh * G) * HD + sub * 8;
+    const uint16_t *qrow = a.qkv + (size_t)w.row0 * a.ld_qkv + (w.kvh * G) * HD + sub * 8;
 #pragma unroll
     for (int h = 0; h < G; ++h) q[h] = *(const u32x4_t *)(qrow + h * HD);
     float sc[NL][G];
@@ -530,7 +528,7 @@ __device__ void decode_path(const AttnArgs &a, const AttnWork &w, DecodeSmem<HD,
     }
   }
   __syncthreads();
-  finish_decode<HD, G>(a, w, it, sm.o, sm.ml);
+  finish_decode<HD, G>(a, w, sm.o, sm.ml);
 }
 
 // Decode work, head dims 64 and 128: keys [k0, k1) (at most DEC_SPLIT_MAX)
@@ -571,16 +569,15 @@ __device__ void decode_mfma_path(const AttnArgs &a, const AttnWork &w, DecodeMfm
   constexpr int NL = 16 / KPI;  // keys per lane per block (V)
   constexpr int NJ = HD / 32;   // MFMA k-slices
   static_assert(NL % 2 == 0, "key pairs");
-  const DevItem it = a.items[w.item];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int pi0 = page_of(a, w.k0);
   const int npg = page_of(a, w.k1 - 1) - pi0 + 1;
-  for (int t = threadIdx.x; t < npg; t += 256) sm.pages[t] = a.page_ids[it.page_off + pi0 + t];
+  for (int t = threadIdx.x; t < npg; t += 256) sm.pages[t] = a.page_ids[w.page_off + pi0 + t];
   const int qh = lane & 15, qg = lane >> 4;
   u32x4_t q[NJ];
   {
     const uint16_t *qrow =
-        a.qkv + (size_t)it.row0 * a.ld_qkv + (size_t)(w.kvh * G + (qh < G ? qh : 0)) * HD + qg * 8;
+        a.qkv + (size_t)w.row0 * a.ld_qkv + (size_t)(w.kvh * G + (qh < G ? qh : 0)) * HD + qg * 8;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -719,7 +716,7 @@ __device__ void decode_mfma_path(const AttnArgs &a, const AttnWork &w, DecodeMfm
     sm.ml[wave][qh][1] = lt;
   }
   __syncthreads();
-  finish_decode<HD, G>(a, w, it, sm.o, sm.ml);
+  finish_decode<HD, G>(a, w, sm.o, sm.ml);
 }
 
 // One launch over the whole work list: each workgroup runs the chunk path

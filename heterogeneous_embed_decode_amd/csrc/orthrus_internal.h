@@ -25,9 +25,14 @@ orthrus_status validate_and_pack(const orthrus_model_cfg &cfg, const orthrus_bat
 //  DECODE: the decode row of `item` for KV head `kvh` against keys
 //          [k0, k1); the workgroup writes partial `part`.
 enum { WORK_CHUNK = 0, WORK_DECODE = 1 };
+// The entry also carries its item's first row, context and page-list
+// offset, so a workgroup starts its page and K/V loads from the entry alone
+// (one dependent load fewer than reading the item record first).
 struct AttnWork {
   int32_t type, item, kvh, q0, qn, k0, k1, part;
+  int32_t row0, ctx, page_off, pad;
 };
+static_assert(sizeof(AttnWork) == 48, "work entries are 12 int32 words");
 // Per-item device record used by the attention and combine kernels.
 struct DevItem {
   int32_t row0, n, ctx, page_off, kind, part0, n_parts, pad;

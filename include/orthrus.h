@@ -217,8 +217,8 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch,
  * on from module load to process end (its address is resolved once per
  * device by orthrus_create), and the call never calls hipMalloc, hipFree,
  * hipHostMalloc or any allocating routine.  Limits: at most 4 MiB of step
- * metadata (about 3 int32 words per row, the page ids, and 8 words per
- * item and per attention work entry: one per 128/(Hq/Hkv) rows of a chunk
+ * metadata (about 3 int32 words per row, the page ids, 8 words per item
+ * and 12 per attention work entry: one per 128/(Hq/Hkv) rows of a chunk
  * per KV head, one per decode split per KV head) and 60 MiB of decode
  * partial results ((Hq/Hkv) * (2 + head_dim) * 4 bytes per decode split
  * per KV head; decode rows split their keys in pieces of 128 to 512);
