@@ -1,8 +1,8 @@
 """Decode attention through orthrus_step against the oracle: decode-heavy
 batches whose sizes select each decode split length (512, 256 and 128 keys
 per workgroup), every grouped-query ratio at head dims 64 and 128, page
-sizes that do and do not divide the 16-key blocks, and contexts on block
-and split boundaries.  Weights are drawn wider than the model default
+sizes that do and do not divide the 16-key blocks (5, 7, 16, 32, 64, 128),
+and contexts on block and split boundaries.  Weights are drawn wider than the model default
 (std 0.05) so that attention is far from uniform and its output is not
 lost under the residual stream."""
 
@@ -81,6 +81,19 @@ CASES = [
                     vocab=300, page_size=5, rope_theta=1e6),
      list(np.random.default_rng(6).integers(1, 900, 90)) + [0, 4, 5, 6],
      []),
+    # pages of 64 keys (one page per 64-key chunk tile: the page-stride
+    # addressing of whole tiles) and of 128 keys (larger than a tile: the
+    # per-key form), with embedding chunks at several contexts
+    ("hd128-g4-ps64-split128",
+     sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn_dim=256,
+                    vocab=300, page_size=64, rope_theta=1e6),
+     list(np.random.default_rng(7).integers(300, 1200, 100)) + [63, 64, 65, 127, 128],
+     [(200, 0), (130, 64), (77, 300)]),
+    ("hd64-g2-ps128-split256",
+     sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=4, head_dim=64, ffn_dim=256,
+                    vocab=300, page_size=128, rope_theta=1e4),
+     list(np.random.default_rng(8).integers(200, 1500, 150)) + [127, 128, 129, 255, 256],
+     [(150, 0), (100, 128), (65, 1000)]),
 ]
 
 
