@@ -20,8 +20,9 @@
  *  - bf16 is IEEE bfloat16 stored as 16-bit patterns; fp32 is IEEE binary32.
  *  - Linear weights are row-major [out_features][in_features].
  *  - K and V caches are each [n_layers][n_pages][n_kv_heads][page_size]
- *    [head_dim] bf16 (fp32 for models of dtype ORTHRUS_F32).  Token position p of an item lives in page
- *    page_ids[page_off + p / page_size] at in-page offset p % page_size.
+ *    [head_dim] bf16 (fp32 for models of dtype ORTHRUS_F32).  Token
+ *    position p of an item lives in page page_ids[page_off + p / page_size]
+ *    at in-page offset p % page_size.
  *  - Nothing throws across this ABI.  Validation runs before any device
  *    work; on a non-OK status no device memory has been touched.
  */
@@ -170,8 +171,9 @@ orthrus_status orthrus_pack(const orthrus_model_cfg *cfg, const orthrus_batch *b
 
 /* Create an engine bound to the current HIP device.  Copies cfg and the
  * weight pointer table; allocates the workspace for max_tokens/max_items.
- * k_pages / v_pages: device bf16 KV pools (layout above), read and written
- * by every step.  Returns EINVAL for an unknown dtype or unsupported shapes (head_dim not in
+ * k_pages / v_pages: device KV pools (layout above; bf16, or fp32 for
+ * ORTHRUS_F32), read and written by every step.  Returns EINVAL for an
+ * unknown dtype or unsupported shapes (head_dim not in
  * {16,32,64,128}, n_q_heads not a multiple of n_kv_heads, d_model above
  * 8192, d_model, Hq*hd, ffn_dim not multiples of 8, lora_rank not a
  * multiple of 8, or a step operand of 2 GiB or more: max_tokens rows of
