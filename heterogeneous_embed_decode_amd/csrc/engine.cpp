@@ -565,7 +565,7 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
          "gemm_qkv");
     LCHK(launch_rope_kv(eng->qkv, d_pos, d_slot, eng->inv_freq, kc, vc, T, Hq, Hkv, hd, c.page_size, s),
          "rope_kv");
-    LCHK(launch_attn_ragged(eng->qkv, qkvd, kc, vc, d_pages, d_items, d_work, n_chunk + n_dec_work, part_ml,
+    LCHK(launch_attn_ragged(eng->qkv, qkvd, kc, vc, d_pages, d_work, n_chunk + n_dec_work, part_ml,
                             part_o, eng->o, qd, Hq, Hkv, hd, c.page_size, s),
          "attn_ragged");
     if (multi_split)

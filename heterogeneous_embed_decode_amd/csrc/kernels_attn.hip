@@ -39,7 +39,6 @@ struct AttnArgs {
   const uint16_t *kc;
   const uint16_t *vc;
   const int32_t *page_ids;
-  const DevItem *items;
   const AttnWork *work;
   float *part_ml;
   float *part_o;
@@ -828,10 +827,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const DevItem *items,
 }
 
 static AttnArgs attn_args(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
-                          const int32_t *page_ids, const DevItem *items, const AttnWork *work, float *part_ml,
+                          const int32_t *page_ids, const AttnWork *work, float *part_ml,
                           float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps) {
   AttnArgs a;
-  a.qkv = qkv; a.kc = kc; a.vc = vc; a.page_ids = page_ids; a.items = items; a.work = work;
+  a.qkv = qkv; a.kc = kc; a.vc = vc; a.page_ids = page_ids; a.work = work;
   a.part_ml = part_ml; a.part_o = part_o; a.o = o;
   a.ld_qkv = ld_qkv; a.ld_o = ld_o; a.Hq = Hq; a.Hkv = Hkv; a.ps = ps;
   a.ps_log2 = (ps & (ps - 1)) == 0 ? __builtin_ctz((unsigned)ps) : -1;
@@ -853,12 +852,11 @@ static int launch_ragged_hd(const AttnArgs &a, int n_work, int G, hipStream_t s)
 }
 
 int launch_attn_ragged(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
-                       const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
+                       const int32_t *page_ids, const AttnWork *work, int n_work,
                        float *part_ml, float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps,
                        void *stream) {
   if (n_work <= 0) return 0;
-  const AttnArgs a = attn_args(qkv, ld_qkv, kc, vc, page_ids, items, work, part_ml, part_o, o, ld_o, Hq, Hkv,
-                               hd, ps);
+  const AttnArgs a = attn_args(qkv, ld_qkv, kc, vc, page_ids, work, part_ml, part_o, o, ld_o, Hq, Hkv, hd, ps);
   const int G = Hq / Hkv;
   hipStream_t s = (hipStream_t)stream;
   switch (hd) {

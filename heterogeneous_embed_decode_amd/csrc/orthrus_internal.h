@@ -91,7 +91,7 @@ int launch_rope_kv(uint16_t *qkv, const int32_t *pos, const int32_t *slot,
                    int hd, int ps, void *stream);
 // one launch over the work list (chunk entries first, then decode entries)
 int launch_attn_ragged(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, const uint16_t *vc,
-                       const int32_t *page_ids, const DevItem *items, const AttnWork *work, int n_work,
+                       const int32_t *page_ids, const AttnWork *work, int n_work,
                        float *part_ml, float *part_o, uint16_t *o, int ld_o, int Hq, int Hkv, int hd, int ps,
                        void *stream);
 int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_dec,

@@ -107,3 +107,53 @@ def sample(logits: np.ndarray, temperature=None, top_p=None, uniforms=None) -> n
         p = 1.0 if top_p is None else float(np.float32(top_p[i]))
         out[i] = sample_row(logits[i], T, p, int(uniforms[i]) if T > 0 else 0)
     return out
+
+
+def sample_exact_row(l: np.ndarray, temperature: float, top_p: float, U: int, margin: float = None):
+    """The textbook definition the readings above approximate, in fp64:
+    softmax weights e^((l_i - max) / T), the nucleus as the smallest set of
+    most probable tokens (lower index first among equal probabilities)
+    whose probability reaches P16 / 65536, and the draw x = (U / 2^32) times
+    the nucleus mass, taking the first token in index order whose running
+    nucleus mass exceeds x.  Returns (token, decided): decided is False when
+    the draw lies within `margin` (relative to the nucleus mass) of a
+    boundary between two tokens, or the nucleus edge within `margin` of the
+    target or of a near-tie, where the fp32 weights of the readings may
+    legitimately pick a neighbour.  The default margin is the readings'
+    error bound: each fp32 weight within about 5e-6 of e^((l - max) / T)
+    (the Taylor polynomial and the fp32 rounding of t, doubled here), and
+    the floor and the zero weights below 2^-30 of the maximum costing at
+    most V / 2^30 of the mass each.  Used to check the readings and the GPU
+    sampler against the definition, not to replace them."""
+    l = np.asarray(l, np.float32).astype(np.float64)
+    if margin is None:
+        margin = 1e-5 + 2.0 * l.size / 2.0 ** 30
+    if not temperature > 0:
+        return int(np.argmax(l)), True
+    w = np.exp((l - l.max()) / float(np.float32(temperature)))
+    Z = float(w.sum())
+    P16 = min(65536, max(1, int(round(float(top_p) * 65536))))
+    decided = True
+    if P16 == 65536:
+        member = np.ones(l.size, bool)
+    else:
+        thr = P16 / 65536.0 * Z
+        order = np.lexsort((np.arange(l.size), -w))          # by weight descending, then index
+        ws = w[order]
+        cum = np.cumsum(ws)
+        k = int(np.searchsorted(cum, thr, side="left"))      # nucleus = order[:k + 1]
+        k = min(k, l.size - 1)
+        if abs(cum[k] - thr) < margin * Z or (k > 0 and abs(cum[k - 1] - thr) < margin * Z):
+            decided = False
+        if k + 1 < l.size and 0.0 < ws[k] - ws[k + 1] < margin * ws[k]:
+            decided = False
+        member = np.zeros(l.size, bool)
+        member[order[:k + 1]] = True
+    run = np.cumsum(np.where(member, w, 0.0))
+    M = float(run[-1])
+    x = int(U) / 2.0 ** 32 * M
+    tok = int(np.searchsorted(run, x, side="right"))
+    edges = run[member]
+    if np.min(np.abs(edges - x)) < margin * M:
+        decided = False
+    return min(tok, l.size - 1), decided

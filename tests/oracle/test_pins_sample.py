@@ -126,3 +126,27 @@ def test_degenerate_temperatures_and_sizes():
     out = sample(L, np.array([0, 1, 0, 1e-30], np.float32), np.ones(4, np.float32),
                  np.array([0, 7, 0, 9], np.uint32))
     assert out[0] == np.argmax(L[0]) and out[2] == np.argmax(L[2]) and out[3] == np.argmax(L[3])
+
+
+def test_reading_matches_exact_definition_away_from_boundaries():
+    """The readings (fp32 Taylor weights, integer nucleus and draw) pick the
+    token of the textbook definition (fp64 softmax with temperature, top-p
+    nucleus, inverse-CDF draw in index order) on every draw that is not
+    within the readings' error bound of a boundary; the bound leaves most
+    draws decided."""
+    from oracle.sample import sample_exact_row
+    rng = np.random.default_rng(21)
+    decided = agree = total = 0
+    for _ in range(500):
+        V = int(rng.choice([2, 37, 1000, 5000]))
+        l = (rng.standard_normal(V) * rng.choice([1.0, 3.0])).astype(np.float32)
+        T = float(rng.choice([0.0, 0.3, 0.7, 1.0, 1.6]))
+        p = float(rng.choice([0.05, 0.5, 0.9, 0.99, 1.0]))
+        U = int(rng.integers(0, 2 ** 32))
+        tok, ok = sample_exact_row(l, T, p, U)
+        total += 1
+        if ok:
+            decided += 1
+            agree += tok == sample_row(l, T, p, U if T > 0 else 0)
+    assert agree == decided
+    assert decided > 0.8 * total, (decided, total)
