@@ -35,13 +35,15 @@ def test_buffered_head_keeps_rows_and_means_them():
     position (against the oracle), and the emitted vector is the mean of
     exactly those buffered rows (checked against the GPU's own buffer in
     fp64, so the head's arithmetic is checked tightly); a request longer
-    than the buffer is refused before any device work."""
+    than the buffer is refused before any device work.  Two other heads
+    (max pooling, attention pooling with a fixed query) run over the GPU's
+    buffer agree with the same heads over the oracle's buffer."""
     cfg = sm.TINY.with_(lora_rank=8)
     bits = sm.make_weights(cfg, seed=6, gain_std=0.1)
     _, batches, n_pages = wl.tiny_workload(cfg=cfg, pool_kind=wl.POOL_BUFFER)
     dev, orc = make_pair(cfg, n_pages, bits, buf_rows=48)
     pool = orc[2]
-    from tests._util import rel_l2
+    from tests._util import rel_l2, cosine
     for s, b in enumerate(batches):
         got, ref, _ = run_and_compare(cfg, dev, orc, b, tag=f"buffer step={s}")
         buf = dev.pool_buf.cpu().numpy()
@@ -57,6 +59,22 @@ def test_buffered_head_keeps_rows_and_means_them():
                 mean = buf[it.pool_slot, :n].astype(np.float64).mean(axis=0)
                 np.testing.assert_allclose(got["emb"][k], mean, rtol=1e-5, atol=1e-6)
                 k += 1
+                # heads other than the built-in mean, run by the caller over
+                # the buffer (the point of keeping every row): max pooling and
+                # attention pooling with a fixed query, against the same heads
+                # over the oracle's buffered hidden states
+                rows_g = buf[it.pool_slot, :n].astype(np.float64)
+                rows_o = np.asarray(pool["buf"][it.pool_slot, :n], np.float64)
+                qv = np.random.default_rng(it.pool_slot).standard_normal(cfg.d_model)
+
+                def attn_pool(r):
+                    a = r @ qv / np.sqrt(cfg.d_model)
+                    a = np.exp(a - a.max())
+                    return (a / a.sum()) @ r
+
+                for head in (lambda r: r.max(axis=0), attn_pool):
+                    hg, ho = head(rows_g), head(rows_o)
+                    assert rel_l2(hg, ho) < 2e-2 and cosine(hg, ho) > 0.999
     # a BUFFER item reaching past buf_rows: ECAPACITY, nothing launched
     bb = wl.BatchBuilder(cfg, wl.PageAllocator(n_pages, seed=1))
     bb.add(wl.Request(7, wl.EMBED, list(range(1, 50)), pool_slot=0, pool_kind=wl.POOL_BUFFER))
