@@ -45,7 +45,7 @@ constexpr int DEC_SPLIT_MIN = 128;   // keys per decode workgroup, head dims 64 
 constexpr int DEC_SPLIT_MAX = 512;   // .. 512, the largest that still gives enough workgroups
 constexpr int DEC_MIN_WGS = 2048;    // decode workgroups wanted before a larger split is taken
 
-// keys per decode workgroup the decode kernel accepts for a head dim
+// keys per decode workgroup the decode path accepts for a head dim
 int decode_split_limit(int hd);
 
 // Work list: chunk entries (heaviest first), then decode entries;
