@@ -61,8 +61,13 @@ def kernel_work(cfg, batch, meta):
     chunk_bytes = 2.0 * 2 * kvd * sum(it.ctx_len + it.n_tokens for it in batch.items if it.kind != 2)
     dec_flops = 4.0 * hd * cfg.n_q_heads * dec_keys
     dec_bytes = 2.0 * 2 * kvd * dec_keys
+    qkv_work = (2.0 * T * qkvd * d + 2.0 * TE * r * qkvd, 2.0 * (T * d + qkvd * d + T * qkvd))
     return {
-        "gemm_qkv": (2.0 * T * qkvd * d + 2.0 * TE * r * qkvd, 2.0 * (T * d + qkvd * d + T * qkvd)),
+        "gemm_qkv": qkv_work,
+        # the same projection with RoPE and the KV append in its epilogue:
+        # the same flops, plus the step's cos/sin table read once
+        "gemm_qkv_rope": (qkv_work[0], qkv_work[1] + 4.0 * T * hd),
+        "rope_table": (0.0, 4.0 * T * hd + 4.0 * T),
         "gemm_o": (2.0 * T * d * qd + 2.0 * TE * r * d, 2.0 * (T * qd + d * qd) + 8.0 * T * d),
         "gemm_gate_up": (2.0 * T * 2 * F * d, 2.0 * (T * d + 2 * F * d + T * F)),
         "gemm_down": (2.0 * T * d * F, 2.0 * (T * F + d * F) + 8.0 * T * d),
@@ -74,6 +79,13 @@ def kernel_work(cfg, batch, meta):
         "lora_shrink_o": (2.0 * TE * r * qd, 2.0 * (TE * qd + r * qd)),
         "pool": (0.0, pool_bytes(cfg, batch)),
     }
+
+
+def qkv_rope_fused(cfg, T):
+    """Whether the library runs RoPE and the KV append in the QKV
+    projection's epilogue for a batch of T rows (head dim 128, an even
+    number of q and of KV heads, at least 512 rows)."""
+    return cfg.head_dim == 128 and T >= 512 and cfg.n_q_heads % 2 == 0 and cfg.n_kv_heads % 2 == 0
 
 
 def step_roofline_ms(cfg, batch, meta):
@@ -95,7 +107,12 @@ def step_roofline_ms(cfg, batch, meta):
         per_layer += ["lora_shrink_qkv", "lora_shrink_o"]
     terms = {k: L * t(*w[k]) for k in per_layer}
     terms["rmsnorm"] = L * 2 * t(0.0, T * d * (4.0 + 2.0))
-    terms["rope_kv"] = L * t(0.0, 2.0 * T * (cfg.q_dim + cfg.kv_dim) * 2 + 2.0 * T * 2 * cfg.kv_dim)
+    if qkv_rope_fused(cfg, T):
+        # RoPE and the KV append run inside the QKV projection, which is
+        # matrix-bound; the step builds one cos/sin table
+        terms["rope_table"] = t(*w["rope_table"])
+    else:
+        terms["rope_kv"] = L * t(0.0, 2.0 * T * (cfg.q_dim + cfg.kv_dim) * 2 + 2.0 * T * 2 * cfg.kv_dim)
     terms["final_norm"] = t(0.0, T * d * 4.0 + (meta["n_embed_rows"] + meta["n_logits"]) * d * 4.0)
     terms["lm_head"] = t(*w["lm_head"])
     terms["pool"] = t(*w["pool"])

@@ -26,6 +26,7 @@ struct orthrus_engine {
   float *hf = nullptr;
   uint16_t *hl = nullptr;
   double *inv_freq = nullptr;
+  float *rope_cs = nullptr;  // [T][head_dim] cos/sin table of the step (bf16 models)
   float *part_ml = nullptr, *part_o = nullptr;
   size_t part_cap = 0;  // in split units
   int32_t *meta_dev = nullptr;
@@ -178,7 +179,7 @@ static void free_all(orthrus_engine *e) {
   for (auto ev : e->ev_free) (void)hipEventDestroy(ev);
   e->ev_free.clear();
   void *ptrs[] = {e->x, e->h, e->qkv, e->o, e->act, e->U, e->hf, e->hl, e->inv_freq,
-                  e->part_ml, e->part_o, e->meta_dev};
+                  e->rope_cs, e->part_ml, e->part_o, e->meta_dev};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   if (e->meta_host) (void)hipHostFree(e->meta_host);
@@ -254,6 +255,7 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
       {(void **)&eng->hf, T * d * 4},
       {(void **)&eng->hl, T * d * es},
       {(void **)&eng->inv_freq, (size_t)hd / 2 * 8},
+      {(void **)&eng->rope_cs, T * hd * 4},
   };
   for (auto &a : allocs)
     if ((r = hipMalloc(a.p, a.bytes)) != hipSuccess) return bail(ORTHRUS_ENOMEM, "hipMalloc", r);
@@ -543,6 +545,15 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
                            1.f, nullptr, 0, nullptr, 0, 0, 0, 0, s),
            "lm_head_f32");
   } else {
+  // RoPE and the KV append run in the QKV projection's epilogue where its
+  // shape allows, from one cos/sin table per step
+  const bool fuse_rope = qkv_rope_fusable(T, Hq, Hkv, hd);
+  RopeKv rk{};
+  if (fuse_rope) {
+    LCHK(launch_rope_table(d_pos, eng->inv_freq, eng->rope_cs, T, hd, s), "rope_table");
+    rk.cs = eng->rope_cs; rk.slot = d_slot;
+    rk.n_q_heads = Hq; rk.n_kv_heads = Hkv; rk.page_size = c.page_size;
+  }
   for (int l = 0; l < c.n_layers; ++l) {
     const orthrus_layer_w &L = eng->layers[l];
     uint16_t *kc = eng->kc + (size_t)l * layer_kv, *vc = eng->vc + (size_t)l * layer_kv;
@@ -560,11 +571,18 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
       la.U = eng->U; la.ldu = 3 * r; la.Bx = (const uint16_t *)L.lora_b_qkv; la.r = r; la.rows = TE;
       la.sec1 = qd; la.sec2 = qd + kvd;
     }
-    LCHK(launch_gemm(eng->h, d, (const uint16_t *)L.w_qkv, d, eng->qkv, qkvd, T, qkvd, d, EPI_BF16, 0, 1.f,
-                     lora ? &la : nullptr, s),
-         "gemm_qkv");
-    LCHK(launch_rope_kv(eng->qkv, d_pos, d_slot, eng->inv_freq, kc, vc, T, Hq, Hkv, hd, c.page_size, s),
-         "rope_kv");
+    if (fuse_rope) {
+      rk.kc = kc; rk.vc = vc;
+      LCHK(launch_gemm_qkv_rope(eng->h, d, (const uint16_t *)L.w_qkv, d, eng->qkv, qkvd, T, d,
+                                lora ? &la : nullptr, rk, s),
+           "gemm_qkv_rope");
+    } else {
+      LCHK(launch_gemm(eng->h, d, (const uint16_t *)L.w_qkv, d, eng->qkv, qkvd, T, qkvd, d, EPI_BF16, 0, 1.f,
+                       lora ? &la : nullptr, s),
+           "gemm_qkv");
+      LCHK(launch_rope_kv(eng->qkv, d_pos, d_slot, eng->inv_freq, kc, vc, T, Hq, Hkv, hd, c.page_size, s),
+           "rope_kv");
+    }
     LCHK(launch_attn_ragged(eng->qkv, qkvd, kc, vc, d_pages, d_work, n_chunk + n_dec_work, part_ml,
                             part_o, eng->o, qd, Hq, Hkv, hd, c.page_size, s),
          "attn_ragged");

@@ -34,6 +34,11 @@ struct GemmArgs {
   // the grid size, whole tiles first and the rest as stream-K slices
   int sk_grid;
   int group_m;  // tile rows per group of the tile order (0 = default)
+  // QKV epilogue only (head dim 128)
+  const float *rope_cs;
+  const int32_t *slot;
+  uint16_t *kc, *vc;
+  int q_cols, kv_cols, n_kv, ps;
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -417,6 +422,105 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     }
   };
 
+  // QKV epilogue (Efficient Iterative Retrieval with Heterogeneous
+  // Batching, §3.1: every row of the batch goes through the same projection;
+  // its keys and values enter the paged cache).  A 256-column tile holds two
+  // whole heads of one section (q, k or v; head dim 128).  The rotate-half
+  // partner of dim i < 64 is dim i + 64, which sits in another wave's
+  // accumulators, so the tile goes through LDS in fp32, 128 rows at a time
+  // ([row][col], col XOR 32 on rows with bit 2 set: the two 32-lane halves
+  // of a store land on different banks, and a 16-lane read of 64
+  // consecutive columns stays conflict-free).  Then thread t (of 512)
+  // rotates 4 pairs (dims 4 (t % 16) .. +3 and their partners) of both
+  // heads on rows t / 16 + 32 k: out_a = a cos - b sin, out_b = b cos + a sin,
+  // one rounding to bf16, and stores 8 bytes per half head, 16 lanes per
+  // 128-byte run: q into qkv, k and v into the row's KV page slot.  The
+  // rows' cos/sin and KV slots are loaded before the LDS exchange that
+  // precedes their use, so their latency overlaps it.
+  auto qkv_epilogue = [&]() {
+    static_assert(EPI != EPI_QKV || (BM == 256 && BN == 256 && WM == 2 && WN == 4 && MT == 32),
+                  "the QKV epilogue assumes 256x256 tiles on 2x4 waves");
+    constexpr int RP = NT / 16;   // rows covered by one pass of all threads
+    constexpr int NR = 128 / RP;  // rows per thread per half tile
+    static_assert(EPI != EPI_QKV || NR * RP == 128, "whole row passes");
+    float *xs = (float *)smem;  // 128 x 256 fp32 = the 128 KB of the two stages
+    const int sec = n0 < g.q_cols ? 0 : (n0 < g.q_cols + g.kv_cols ? 1 : 2);
+    const int jc = lane & (MT - 1);
+    const int g4 = tid & 15;
+    uint16_t *const dst0 = sec == 0 ? (uint16_t *)g.C : (sec == 1 ? g.kc : g.vc);
+    const int kvh0 = sec == 0 ? 0 : (n0 - g.q_cols - (sec == 2 ? g.kv_cols : 0)) / 128;
+    const size_t head_stride = sec == 0 ? 128 : (size_t)g.ps * 128;
+    float4 cpre[NR] = {}, spre[NR] = {};
+    int spre_slot[NR] = {};
+    auto prefetch = [&](int half) {
+#pragma unroll
+      for (int it = 0; it < NR; ++it) {
+        const int m = min(m0 + half * 128 + (tid >> 4) + RP * it, g.M - 1);
+        if (sec < 2) {
+          cpre[it] = *(const float4 *)(g.rope_cs + (size_t)m * 128 + g4 * 4);
+          spre[it] = *(const float4 *)(g.rope_cs + (size_t)m * 128 + 64 + g4 * 4);
+        }
+        if (sec > 0) spre_slot[it] = g.slot[m];
+      }
+    };
+    prefetch(0);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();  // the stages (or the previous half) are no longer read
+      if (wm == half) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+              const int row = i * MT + (e / 4) * 8 + (lane >> 5) * 4 + (e % 4);
+              const int col = wn * WCN + j * MT + jc;
+              xs[row * 256 + (col ^ (((row >> 2) & 1) << 5))] = g.alpha * acc[i][j][e];
+            }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < NR; ++it) {
+        const int r = (tid >> 4) + RP * it;
+        const int m = m0 + half * 128 + r;
+        const int sw = ((r >> 2) & 1) << 5;
+        size_t rowbase;  // element offset of the row's first head in the tile
+        if (sec == 0) {
+          rowbase = (size_t)m * g.ldc + n0;
+        } else {
+          const int sl = spre_slot[it];
+          const int page = sl / g.ps, off = sl - page * g.ps;
+          rowbase = (((size_t)page * g.n_kv + kvh0) * g.ps + off) * 128;
+        }
+        const float cc[4] = {cpre[it].x, cpre[it].y, cpre[it].z, cpre[it].w};
+        const float ss[4] = {spre[it].x, spre[it].y, spre[it].z, spre[it].w};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int ca = hh * 128 + g4 * 4;
+          const float4 a = *(const float4 *)&xs[r * 256 + (ca ^ sw)];
+          const float4 b = *(const float4 *)&xs[r * 256 + ((ca + 64) ^ sw)];
+          const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+          float oa[4], ob[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            oa[u] = sec < 2 ? av[u] * cc[u] - bv[u] * ss[u] : av[u];
+            ob[u] = sec < 2 ? bv[u] * cc[u] + av[u] * ss[u] : bv[u];
+          }
+          if (m < g.M) {
+            uint16_t *dst = dst0 + rowbase + hh * head_stride + g4 * 4;
+            uint2 wa, wb;
+            wa.x = pack_bf2(oa[0], oa[1]); wa.y = pack_bf2(oa[2], oa[3]);
+            wb.x = pack_bf2(ob[0], ob[1]); wb.y = pack_bf2(ob[2], ob[3]);
+            *(uint2 *)dst = wa;
+            *(uint2 *)(dst + 64) = wb;
+          }
+        }
+      }
+      if (half == 0) prefetch(1);
+    }
+  };
+
   if (g.sk_grid == 0) {
     set_tile(xcd_remap(blockIdx.x, P));
     zero_acc();
@@ -425,7 +529,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
       __builtin_amdgcn_s_barrier();  // all waves are done with the last stage
       run_phase(1, g.ldu, 0, (g.ldu + BK - 1) / BK);
     }
-    epilogue(true);
+    if constexpr (EPI == EPI_QKV) qkv_epilogue();
+    else epilogue(true);
   } else if (EPI == EPI_RESID) {
     // residual projections on a grid of sk_grid workgroups (one per CU):
     // whole tiles first, in rounds of sk_grid consecutive tiles of the
@@ -567,6 +672,30 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
       return launch_cfg<128, 64, 2, 2, 64, 2, EPI_SWIGLU>(a, s);
   }
   return (int)hipErrorInvalidValue;
+}
+
+// The fused QKV epilogue needs head dim 128 and q and k/v sections of whole
+// 256-column tiles; below 512 rows the projection takes smaller tiles.
+bool qkv_rope_fusable(int M, int Hq, int Hkv, int hd) {
+  return hd == 128 && M >= 512 && Hq % 2 == 0 && Hkv % 2 == 0 && Hkv > 0;
+}
+
+int launch_gemm_qkv_rope(const uint16_t *A, int lda, const uint16_t *B, int ldb, uint16_t *qkv, int ldc, int M,
+                         int K, const LoraArgs *lora, const RopeKv &rk, void *stream) {
+  if (!qkv_rope_fusable(M, rk.n_q_heads, rk.n_kv_heads, 128) || !rk.cs || !rk.slot || !rk.kc || !rk.vc ||
+      rk.page_size <= 0 || ldc != (rk.n_q_heads + 2 * rk.n_kv_heads) * 128)
+    return (int)hipErrorInvalidValue;
+  GemmArgs a{};
+  a.A = A; a.B = B; a.C = qkv;
+  a.lda = lda; a.ldb = ldb; a.ldc = ldc; a.M = M; a.N = ldc; a.K = K;
+  a.alpha = 1.f;
+  if (lora && lora->U && lora->rows > 0 && lora->r > 0) {
+    a.U = lora->U; a.Bx = lora->Bx; a.ldu = lora->ldu; a.r = lora->r; a.lrows = lora->rows;
+    a.sec1 = lora->sec1; a.sec2 = lora->sec2;
+  }
+  a.rope_cs = rk.cs; a.slot = rk.slot; a.kc = rk.kc; a.vc = rk.vc;
+  a.q_cols = rk.n_q_heads * 128; a.kv_cols = rk.n_kv_heads * 128; a.n_kv = rk.n_kv_heads; a.ps = rk.page_size;
+  return launch_cfg<256, 256, 2, 4, 64, 2, EPI_QKV>(a, (hipStream_t)stream);
 }
 
 }  // namespace orthrus

@@ -141,6 +141,20 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(uint16_t *qkv, const int32
   }
 }
 
+// The step's rotation table for the QKV projection's epilogue: row t holds
+// cos(pos[t] * inv_freq[i]) for i < hd/2, then the sines; the angles are
+// formed in fp64 as in rope_kv_kernel, so both paths rotate by the same
+// fp32 values.  One table serves every layer of the step.
+__global__ __launch_bounds__(64) void rope_table_kernel(const int32_t *pos, const double *inv_freq, float *cs,
+                                                        int hd) {
+  const int t = blockIdx.x, half = hd / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const double ang = (double)pos[t] * inv_freq[i];
+    cs[(size_t)t * hd + i] = (float)cos(ang);
+    cs[(size_t)t * hd + half + i] = (float)sin(ang);
+  }
+}
+
 // Final RMSNorm for the rows the outputs need: blocks [0, n_embed) normalise
 // embedding rows (emb_rows[b], or row b when emb_rows is null) into hf at
 // their row (fp32, pooler input); blocks [n_embed, n_embed + n_logit)
@@ -338,6 +352,13 @@ int launch_embed_rmsnorm(const int32_t *tok, const uint16_t *E, const uint16_t *
 int launch_rmsnorm(const float *x, const uint16_t *g, uint16_t *h, int T, int d, float eps, void *stream) {
   if (T <= 0) return 0;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, (hipStream_t)stream, x, g, h, d, eps);
+  ORTHRUS_LAUNCH_CHECK();
+  return 0;
+}
+
+int launch_rope_table(const int32_t *pos, const double *inv_freq, float *cs, int T, int hd, void *stream) {
+  if (T <= 0) return 0;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(T), dim3(64), 0, (hipStream_t)stream, pos, inv_freq, cs, hd);
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }

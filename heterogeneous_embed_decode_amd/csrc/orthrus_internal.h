@@ -76,11 +76,28 @@ struct LoraArgs {
   int sec1 = 0, sec2 = 0;        // column n in section 0 if n < sec1, 1 if < sec2, else 2
 };
 
-enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
+enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
 
 int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C, int ldc,
                 int M, int N, int K, int epi, int b_up_row, float alpha,
                 const LoraArgs *lora, void *stream);
+
+// QKV projection with RoPE and the KV append in its epilogue: q (rotated)
+// lands in columns [0, Hq*hd) of qkv, k (rotated) and v at each row's KV
+// slot, columns [Hq*hd, ldc) of qkv are left unwritten.  Only for the
+// shapes qkv_rope_fusable() accepts; the others take launch_gemm followed
+// by launch_rope_kv.
+struct RopeKv {
+  const float *cs = nullptr;      // [M][hd]: cos of the hd/2 angles, then their sin
+  const int32_t *slot = nullptr;  // [M] KV slot of each row
+  uint16_t *kc = nullptr, *vc = nullptr;
+  int n_q_heads = 0, n_kv_heads = 0, page_size = 0;
+};
+bool qkv_rope_fusable(int M, int Hq, int Hkv, int hd);
+int launch_gemm_qkv_rope(const uint16_t *A, int lda, const uint16_t *B, int ldb, uint16_t *qkv, int ldc, int M,
+                         int K, const LoraArgs *lora, const RopeKv &rk, void *stream);
+// cs[t][i] = cos(pos[t] * inv_freq[i]), cs[t][hd/2 + i] = sin(...), angles in fp64
+int launch_rope_table(const int32_t *pos, const double *inv_freq, float *cs, int T, int hd, void *stream);
 
 int launch_embed_rmsnorm(const int32_t *tok, const uint16_t *E, const uint16_t *g, float *x, uint16_t *h,
                          int T, int d, float eps, void *stream);

@@ -141,6 +141,62 @@ def test_random_ragged_batches(seed):
     dev.close()
 
 
+def _exact_rows_batch(cfg, seed):
+    """512 rows: an embedding chunk that starts its request, a prefill chunk
+    after 40 keys and one decode row at context 300 (pages drawn at random)."""
+    rng = np.random.default_rng(seed)
+    ps = cfg.page_size
+    specs = [(wl.EMBED, 300, 0, 1), (wl.PREFILL, 211, 40, 0), (wl.DECODE, 1, 300, 0)]
+    n_pages = sum(-(-(n + c) // ps) for _, n, c, _ in specs) + 3
+    alloc = wl.PageAllocator(n_pages, seed=seed)
+    items, pages = [], []
+    for i, (k, n, c, first) in enumerate(specs):
+        pg = alloc.alloc(-(-(n + c) // ps))
+        items.append(wl.Item(kind=k, req_id=10 + i, n_tokens=n, ctx_len=c, page_off=len(pages), n_pages=len(pg),
+                             pool_slot=3 if k == wl.EMBED else -1, pool_kind=wl.POOL_MEAN if k == wl.EMBED else 0,
+                             is_first=first, is_last=1))
+        pages.extend(pg)
+    toks = rng.integers(0, cfg.vocab, 512).astype(np.int32)
+    return wl.Batch(items, toks, np.asarray(pages, np.int32)), n_pages
+
+
+@pytest.mark.parametrize("case", range(5))
+def test_qkv_projection_with_rope_epilogue(case):
+    """At head dim 128 with an even number of q and KV heads, batches of 512
+    rows or more run RoPE and the KV append in the QKV projection's epilogue
+    (256-column tiles of two whole heads, rows past the last full tile
+    masked).  Ragged row counts, page sizes 5, 16 and 64, the adapter on
+    embedding rows and 1, 2 and 4 grouped heads against the oracle, K/V
+    pages included; case 4 is 511 rows, which takes the separate RoPE
+    kernel, beside case 3 at exactly 512."""
+    cfgs = [sm.ModelConfig(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=128, ffn_dim=384,
+                           vocab=1000, lora_rank=8, page_size=5, rope_theta=1e6),
+            sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn_dim=384,
+                           vocab=1000, lora_rank=16, page_size=16, rope_theta=1e4),
+            sm.ModelConfig(n_layers=1, d_model=384, n_q_heads=4, n_kv_heads=4, head_dim=128, ffn_dim=256,
+                           vocab=700, lora_rank=0, page_size=64, rope_theta=1e6)]
+    if case < 3:
+        cfg = cfgs[case]
+        b, n_pages = wl.random_batch(cfg, (209, 208, 218)[case], max_items=15, max_len=220, max_ctx=500)
+    else:
+        cfg = cfgs[0]
+        b, n_pages = _exact_rows_batch(cfg, 7)
+        if case == 4:
+            it = b.items[1]
+            b.items[1] = wl.Item(kind=it.kind, req_id=it.req_id, n_tokens=it.n_tokens - 1, ctx_len=it.ctx_len,
+                                 page_off=it.page_off, n_pages=it.n_pages, is_last=1)
+            b = wl.Batch(b.items, np.delete(b.token_ids, 400), b.page_ids)
+    print(f"qkv+rope case {case}: rows={b.n_tokens} hd={cfg.head_dim} Hq={cfg.n_q_heads} "
+          f"Hkv={cfg.n_kv_heads} ps={cfg.page_size}", flush=True)
+    assert (b.n_tokens >= 512) == (case != 4)
+    bits = sm.make_weights(cfg, seed=case, gain_std=0.1)
+    kv = wl.synthetic_kv(cfg, n_pages, seed=3)
+    dev, orc = make_pair(cfg, n_pages, bits, kv_bits=kv, max_tokens=2048)
+    seed_pool(dev, orc, case)
+    run_and_compare(cfg, dev, orc, b, tag=f"qkv+rope case={case}")
+    dev.close()
+
+
 @pytest.mark.parametrize("pool_kind", [wl.POOL_LAST, wl.POOL_BUFFER | wl.POOL_L2])
 def test_one_mistral_layer_full_batch(pool_kind):
     # the one-layer batch as bench.py runs it (default last-token pooling, and

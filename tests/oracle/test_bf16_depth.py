@@ -19,7 +19,9 @@ That is why full-depth GPU parity holds each layer to 2e-2 on its own
 of 1.1e-2 * sqrt(layers).  Rounding points emulated: the attention and FFN
 norm outputs, the q/k/v projections, q and k after RoPE, the softmax
 numerators entering P.V (normalised by the fp32 sum), the attention output,
-and the SwiGLU output.
+and the SwiGLU output.  (Batches of 512 rows or more at head dim 128 rotate
+the fp32 projection in its epilogue and round q and k once, after RoPE; the
+emulation keeps the rounding before RoPE too, which can only add error.)
 """
 
 import numpy as np
