@@ -97,7 +97,8 @@ def _load():
     lib.orthrus_destroy.restype = None
     lib.orthrus_gemm_bf16.argtypes = [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.orthrus_gemm_bf16.restype = ctypes.c_int
-    lib.orthrus_lora_shrink_bf16.argtypes = [_vp, _i32, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp]
+    lib.orthrus_lora_shrink_bf16.argtypes = [_vp, _i32, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp,
+                                             ctypes.c_int64, _vp]
     lib.orthrus_lora_shrink_bf16.restype = ctypes.c_int
     lib.orthrus_sample.argtypes = [_vp, ctypes.c_int64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
     lib.orthrus_sample.restype = ctypes.c_int
@@ -236,8 +237,9 @@ def orthrus_gemm_bf16(A, lda, B, ldb, C, ldc, M, N, K, epilogue, b_up_row=0, str
     return LIB.orthrus_gemm_bf16(A, lda, B, ldb, C, ldc, M, N, K, epilogue, b_up_row, stream)
 
 
-def orthrus_lora_shrink_bf16(X, ldx, A, rows, nr, K, scale, U, stream=None) -> int:
-    return LIB.orthrus_lora_shrink_bf16(X, ldx, A, rows, nr, K, scale, U, stream)
+def orthrus_lora_shrink_bf16(X, ldx, A, rows, nr, K, scale, U, workspace=None, workspace_bytes=0,
+                             stream=None) -> int:
+    return LIB.orthrus_lora_shrink_bf16(X, ldx, A, rows, nr, K, scale, U, workspace, workspace_bytes, stream)
 
 
 def orthrus_set_layer_dump(eng, dst, cap_rows) -> int:

@@ -27,6 +27,8 @@ struct orthrus_engine {
   uint16_t *hl = nullptr;
   double *inv_freq = nullptr;
   float *rope_cs = nullptr;  // [T][head_dim] cos/sin table of the step (bf16 models)
+  float *lora_ws = nullptr;  // fp32 partial sums of the adapter shrinks
+  size_t lora_ws_bytes = 0;
   float *part_ml = nullptr, *part_o = nullptr;
   size_t part_cap = 0;  // in split units
   int32_t *meta_dev = nullptr;
@@ -179,7 +181,7 @@ static void free_all(orthrus_engine *e) {
   for (auto ev : e->ev_free) (void)hipEventDestroy(ev);
   e->ev_free.clear();
   void *ptrs[] = {e->x, e->h, e->qkv, e->o, e->act, e->U, e->hf, e->hl, e->inv_freq,
-                  e->rope_cs, e->part_ml, e->part_o, e->meta_dev};
+                  e->rope_cs, e->lora_ws, e->part_ml, e->part_o, e->meta_dev};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   if (e->meta_host) (void)hipHostFree(e->meta_host);
@@ -259,6 +261,20 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
   };
   for (auto &a : allocs)
     if ((r = hipMalloc(a.p, a.bytes)) != hipSuccess) return bail(ORTHRUS_ENOMEM, "hipMalloc", r);
+  if (c.lora_rank > 0 && c.dtype != ORTHRUS_F32) {
+    // the shrinks' split-K partial sums: the most that the QKV (3r columns
+    // over d) or O (r columns over Hq*hd) shrink needs at up to max_tokens
+    // embedding rows (fewer rows take more splits; within a 64-row tile row
+    // the need grows with the rows)
+    for (size_t rows = 64;; rows += 64) {
+      const int rr = (int)std::min(rows, T);
+      eng->lora_ws_bytes = std::max({eng->lora_ws_bytes, lora_shrink_ws_bytes(rr, 3 * c.lora_rank, (int)d),
+                                     lora_shrink_ws_bytes(rr, c.lora_rank, (int)qd)});
+      if ((size_t)rr == T) break;
+    }
+    if (eng->lora_ws_bytes && (r = hipMalloc(&eng->lora_ws, eng->lora_ws_bytes)) != hipSuccess)
+      return bail(ORTHRUS_ENOMEM, "hipMalloc", r);
+  }
   std::vector<double> inv(hd / 2);
   for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / hd);
   if ((r = hipMemcpy(eng->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice)) != hipSuccess)
@@ -566,7 +582,8 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
       LCHK(launch_rmsnorm(eng->x, (const uint16_t *)L.g_attn, eng->h, T, d, c.rms_eps, s), "rmsnorm");
     LoraArgs la{};
     if (lora) {
-      LCHK(launch_lora_shrink(eng->h, d, (const uint16_t *)L.lora_a_qkv, TE, 3 * r, d, c.lora_scale, eng->U, s),
+      LCHK(launch_lora_shrink(eng->h, d, (const uint16_t *)L.lora_a_qkv, TE, 3 * r, d, c.lora_scale, eng->U,
+                              eng->lora_ws, eng->lora_ws_bytes, s),
            "lora_shrink_qkv");
       la.U = eng->U; la.ldu = 3 * r; la.Bx = (const uint16_t *)L.lora_b_qkv; la.r = r; la.rows = TE;
       la.sec1 = qd; la.sec2 = qd + kvd;
@@ -591,7 +608,8 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
                                Hq, Hkv, hd, s),
            "attn_combine");
     if (lora) {
-      LCHK(launch_lora_shrink(eng->o, qd, (const uint16_t *)L.lora_a_o, TE, r, qd, c.lora_scale, eng->U, s),
+      LCHK(launch_lora_shrink(eng->o, qd, (const uint16_t *)L.lora_a_o, TE, r, qd, c.lora_scale, eng->U,
+                              eng->lora_ws, eng->lora_ws_bytes, s),
            "lora_shrink_o");
       la.ldu = r; la.Bx = (const uint16_t *)L.lora_b_o; la.sec1 = d; la.sec2 = d;
     }
@@ -733,13 +751,14 @@ orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int3
 }
 
 orthrus_status orthrus_lora_shrink_bf16(const void *X, int32_t ldx, const void *A, int32_t rows, int32_t nr,
-                                        int32_t K, float scale, void *U, void *stream) {
-  if (rows < 0 || nr < 0 || K < 8 || K % 8 || ldx < K || ldx % 8) return ORTHRUS_EINVAL;
+                                        int32_t K, float scale, void *U, void *workspace, int64_t workspace_bytes,
+                                        void *stream) {
+  if (rows < 0 || nr < 0 || K < 8 || K % 8 || ldx < K || ldx % 8 || workspace_bytes < 0) return ORTHRUS_EINVAL;
   if (rows == 0 || nr == 0) return ORTHRUS_OK;
   if (!X || !A || !U) return ORTHRUS_EINVAL;
   if (!fits_buffer(((size_t)(rows - 1) * ldx + K) * 2) || !fits_buffer((size_t)nr * K * 2)) return ORTHRUS_EINVAL;
   return launch_lora_shrink((const uint16_t *)X, ldx, (const uint16_t *)A, rows, nr, K, scale, (uint16_t *)U,
-                            stream)
+                            (float *)workspace, workspace ? (size_t)workspace_bytes : 0, stream)
              ? ORTHRUS_EHIP
              : ORTHRUS_OK;
 }

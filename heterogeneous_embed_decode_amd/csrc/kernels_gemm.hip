@@ -521,7 +521,19 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
     }
   };
 
-  if (g.sk_grid == 0) {
+  if (g.sk_grid == 0 && gridDim.y > 1) {
+    // K split over gridDim.y (fp32 outputs only): split y runs K-steps
+    // [nk y / ny, nk (y + 1) / ny) of its tile and stores its partial sums
+    // in slab y of C, [y][M][ldc]; the caller adds the slabs in order
+    if constexpr (EPI == EPI_F32) {
+      set_tile(xcd_remap(blockIdx.x, P));
+      zero_acc();
+      const int ny = gridDim.y, y = blockIdx.y;
+      g.C = (float *)g.C + (size_t)y * g.M * g.ldc;
+      run_phase(0, g.K, (int)((long)nk * y / ny), (int)((long)nk * (y + 1) / ny));
+      epilogue(true);
+    }
+  } else if (g.sk_grid == 0) {
     set_tile(xcd_remap(blockIdx.x, P));
     zero_acc();
     run_phase(0, g.K, 0, nk);
@@ -573,7 +585,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int S, int EPI>
-static int launch_cfg(GemmArgs a, hipStream_t s, int sk_grid = 0) {
+static int launch_cfg(GemmArgs a, hipStream_t s, int sk_grid = 0, int k_splits = 1) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (tiles == 0) return 0;
   constexpr int BNB = (EPI == EPI_SWIGLU) ? 2 * BN : BN;
@@ -586,12 +598,12 @@ static int launch_cfg(GemmArgs a, hipStream_t s, int sk_grid = 0) {
     attr_set = true;
   }
   a.sk_grid = sk_grid;
-  hipLaunchKernelGGL(kern, dim3(sk_grid > 0 ? sk_grid : tiles), dim3(WM * WN * 64), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(sk_grid > 0 ? sk_grid : tiles, k_splits), dim3(WM * WN * 64), lds, s, a);
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }
 
-static int cu_count() {
+int gemm_cu_count() {
   static int n = 0;
   if (n == 0) {
     int dev = 0;
@@ -643,8 +655,8 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
       // otherwise one workgroup per tile (measured faster at 512 tiles).
       if (big) {
         const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
-        const int rem = tiles % cu_count();
-        return launch_cfg<256, 256, 4, 2, 64, 2, EPI_RESID>(a, s, rem != 0 && rem < cu_count() / 2 ? cu_count() : 0);
+        const int rem = tiles % gemm_cu_count();
+        return launch_cfg<256, 256, 4, 2, 64, 2, EPI_RESID>(a, s, rem != 0 && rem < gemm_cu_count() / 2 ? gemm_cu_count() : 0);
       }
       if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_RESID>(a, s);
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);
@@ -654,7 +666,7 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
         // 256-row tiles when the full tile rows fill whole rounds; those
         // rows then go to a launch of 64-row tiles instead
         const int tn = (N + 127) / 128, full = M / 256, rest = M - full * 256;
-        const int cus = cu_count();
+        const int cus = gemm_cu_count();
         if (rest > 0 && rest <= 64 && full > 0 &&
             (full * tn + cus - 1) / cus < ((full + 1) * tn + cus - 1) / cus) {
           GemmArgs lo = a;
@@ -672,6 +684,19 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
       return launch_cfg<128, 64, 2, 2, 64, 2, EPI_SWIGLU>(a, s);
   }
   return (int)hipErrorInvalidValue;
+}
+
+// Adapter shrink with K split over `splits` workgroups per 64 x 64 tile:
+// fp32 partial sums into P [splits][rows][nr] (the caller reduces them).
+int launch_gemm_f32_ksplit(const uint16_t *A, int lda, const uint16_t *B, int ldb, float *P, int M, int N, int K,
+                           int splits, void *stream) {
+  if (M <= 0 || N <= 0) return 0;
+  if (splits < 1 || splits > 65535) return (int)hipErrorInvalidValue;
+  GemmArgs a{};
+  a.A = A; a.B = B; a.C = P;
+  a.lda = lda; a.ldb = ldb; a.ldc = N; a.M = M; a.N = N; a.K = K;
+  a.alpha = 1.f;
+  return launch_cfg<64, 64, 2, 2, 64, 4, EPI_F32>(a, (hipStream_t)stream, 0, splits);
 }
 
 // The fused QKV epilogue needs head dim 128 and q and k/v sections of whole

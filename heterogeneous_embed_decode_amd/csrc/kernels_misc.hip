@@ -11,6 +11,8 @@
 #include "device_common.h"
 #include "orthrus_internal.h"
 
+#include <algorithm>
+
 namespace orthrus {
 
 __device__ __forceinline__ float block_sum_256(float v, float *red) {
@@ -403,15 +405,54 @@ namespace orthrus {
 
 // Adapter shrink U = bf16(s * X A^T) for the embedding rows (the LoRA "A"
 // projection; Efficient Iterative Retrieval with Heterogeneous Batching,
-// §2.2 Parameter sharing): a GEMM with few output columns (3 x rank), run
-// on the projection GEMM kernel with the scale folded into its bf16
-// epilogue.  (A streaming kernel that split K over four waves with a deep
-// register ring measured slower on MI355X: 37 us against 15 us for 7168 x
-// 48 x 4096.)
+// §2.2 Parameter sharing): a GEMM with few output columns (3 x rank) and a
+// long K.  With one workgroup per 64 x 64 tile, 7168 rows give only 112
+// workgroups, each streaming its rows over all of K, which leaves most of
+// the chip idle; so K is split over enough workgroups per tile to reach
+// one workgroup per slot of the chip, each storing fp32 partial sums, and a second kernel adds the
+// splits in order, scales and rounds once.  Without a workspace the scale
+// is folded into the GEMM's bf16 epilogue instead.  (A streaming kernel that
+// split K over four waves with a deep register ring measured slower on
+// MI355X: 37 us against 15 us for 7168 x 48 x 4096.)
+static int lora_shrink_splits(int rows, int nr, int K) {
+  const int tiles = ((rows + 63) / 64) * ((nr + 63) / 64);
+  const int nk = (K + 63) / 64;
+  // one round: two 64 x 64 workgroups fit a CU (64 KB of LDS each), and a
+  // split count that spills past the slots doubles the launch (7168 rows:
+  // 5 splits of 112 tiles ran 22 us, 4 splits fill 448 of 512 slots)
+  int s = 2 * gemm_cu_count() / tiles;
+  s = std::min(s, std::min(8, nk / 4));
+  return std::max(s, 1);
+}
+
+size_t lora_shrink_ws_bytes(int rows, int nr, int K) {
+  const int s = lora_shrink_splits(rows, nr, K);
+  return s > 1 ? (size_t)s * rows * nr * 4 : 0;
+}
+
+// U[e] = bf16(scale * (P[0][e] + P[1][e] + ...)), e over rows * nr elements
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float *P, int splits, size_t n, float scale,
+                                                            uint16_t *U) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+    float acc = P[e];
+    for (int y = 1; y < splits; ++y) acc += P[(size_t)y * n + e];
+    U[e] = (uint16_t)f2bf(scale * acc);
+  }
+}
+
 int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, int nr, int K, float scale,
-                       uint16_t *U, void *stream) {
+                       uint16_t *U, float *ws, size_t ws_bytes, void *stream) {
   if (rows <= 0 || nr <= 0) return 0;
-  return launch_gemm(X, ldx, A, K, U, nr, rows, nr, K, EPI_BF16, 0, scale, nullptr, stream);
+  const int splits = lora_shrink_splits(rows, nr, K);
+  if (splits < 2 || !ws || ws_bytes < lora_shrink_ws_bytes(rows, nr, K))
+    return launch_gemm(X, ldx, A, K, U, nr, rows, nr, K, EPI_BF16, 0, scale, nullptr, stream);
+  if (int r = launch_gemm_f32_ksplit(X, ldx, A, K, ws, rows, nr, K, splits, stream)) return r;
+  const size_t n = (size_t)rows * nr;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(ksplit_reduce_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, ws, splits, n, scale, U);
+  ORTHRUS_LAUNCH_CHECK();
+  return 0;
 }
 
 }  // namespace orthrus

@@ -129,8 +129,17 @@ int launch_rope_kv_f32(float *qkv, const int32_t *pos, const int32_t *slot, cons
 int launch_attn_f32(const float *qkv, const float *kc, const float *vc, const int32_t *page_ids,
                     const DevItem *items, const int32_t *row_item, const int32_t *pos, float *o, int T, int Hq,
                     int Hkv, int hd, int ps, void *stream);
+// compute units of the current device (queried once per process)
+int gemm_cu_count();
+int launch_gemm_f32_ksplit(const uint16_t *A, int lda, const uint16_t *B, int ldb, float *P, int M, int N, int K,
+                           int splits, void *stream);
+// U = bf16(scale X A^T).  With a workspace of at least
+// lora_shrink_ws_bytes(rows, nr, K) bytes, K is split over several
+// workgroups per tile (fp32 partials reduced in a fixed order); with less
+// (or none), one workgroup runs a tile's whole K.
+size_t lora_shrink_ws_bytes(int rows, int nr, int K);
 int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, int nr, int K, float scale,
-                       uint16_t *U, void *stream);
+                       uint16_t *U, float *ws, size_t ws_bytes, void *stream);
 int launch_sample(const float *logits, int64_t ld, int n_rows, int V, const float *temperature,
                   const float *top_p, const uint32_t *uniforms, int32_t *tokens, void *stream);
 int launch_hash_fill(uint16_t *dst, uint64_t n, uint32_t seed, uint32_t tensor_id, uint64_t start, void *stream);

@@ -305,14 +305,23 @@ orthrus_status orthrus_gemm_bf16(const void *A, int32_t lda, const void *B, int3
  *  A      device bf16 [nr][K]: the adapter's down-projection, one row per
  *         output column (nr = 3 x rank for QKV, rank for O)
  *  U      device bf16 [rows][nr] out
- * Runs the projection GEMM kernel with `scale` folded into its bf16
- * epilogue (a whole tile's K sum per workgroup, so the result does not
- * depend on timing).  Asynchronous on
- * `stream`; allocates nothing.  EINVAL for rows or nr < 0, K < 8, K % 8,
- * ldx < K, ldx % 8, NULL pointers with rows, nr > 0, or operands spanning
- * 2 GiB or more; EHIP on launch failure. */
+ *  workspace, workspace_bytes
+ *         optional device scratch (NULL or too small: not used).  With
+ *         at least 32 * rows * nr bytes the library may split K over up to
+ *         8 workgroups per 64 x 64 tile (at most two workgroups per compute
+ *         unit in all) and
+ *         add their fp32 partial sums in a fixed order in a second kernel;
+ *         otherwise one workgroup runs a tile's whole K with `scale` folded
+ *         into the GEMM's bf16 epilogue.  Either way the result does not
+ *         depend on timing.  The step uses a workspace it allocates at
+ *         orthrus_create.
+ * Asynchronous on `stream`; allocates nothing.  EINVAL for rows or nr < 0,
+ * K < 8, K % 8, ldx < K, ldx % 8, workspace_bytes < 0, NULL pointers with
+ * rows, nr > 0, or operands spanning 2 GiB or more; EHIP on launch
+ * failure. */
 orthrus_status orthrus_lora_shrink_bf16(const void *X, int32_t ldx, const void *A, int32_t rows,
-                                        int32_t nr, int32_t K, float scale, void *U, void *stream);
+                                        int32_t nr, int32_t K, float scale, void *U, void *workspace,
+                                        int64_t workspace_bytes, void *stream);
 
 /* Next-token choice for logit rows (full text §3.1: the emit stage hands
  * every generation request's last-row logits to the sampler; §2.2

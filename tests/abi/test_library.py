@@ -174,4 +174,5 @@ def test_lora_shrink_rejects_bad_sizes_before_device_work():
     assert hed.orthrus_lora_shrink_bf16(None, 32, p, 1, 1, 32, 1.0, p) == hed.EINVAL    # NULL X
     assert hed.orthrus_lora_shrink_bf16(p, 32, p, 1, 1, 32, 1.0, None) == hed.EINVAL    # NULL U
     assert hed.orthrus_lora_shrink_bf16(p, 1 << 20, p, 1 << 11, 1, 1024, 1.0, p) == hed.EINVAL  # X spans 4 GiB
+    assert hed.orthrus_lora_shrink_bf16(p, 32, p, 1, 1, 32, 1.0, p, p, -1) == hed.EINVAL  # workspace bytes < 0
     assert hed.orthrus_lora_shrink_bf16(None, 32, None, 0, 1, 32, 1.0, None) == hed.OK  # nothing to do

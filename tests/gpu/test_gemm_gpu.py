@@ -99,9 +99,13 @@ SHRINK = [(1, 16, 32, 1.0, 0), (15, 48, 64, 0.5, 0), (17, 24, 96, 2.0, 8), (300,
           (200, 80, 256, 1.0, 0), (50, 16, 72, 1.0, 0)]
 
 
+@pytest.mark.parametrize("ws", [False, True], ids=["one_pass", "k_split"])
 @pytest.mark.parametrize("rows,nr,K,scale,pad", SHRINK)
-def test_lora_shrink(rows, nr, K, scale, pad):
-    print(f"shrink rows={rows} nr={nr} K={K} scale={scale} pad={pad}", flush=True)
+def test_lora_shrink(rows, nr, K, scale, pad, ws):
+    """With a workspace the library splits K over several workgroups per
+    tile when the tiles are too few to fill the chip (the 300-, 4096- and
+    7168-row cases at K = 4096) and adds the fp32 partials in order."""
+    print(f"shrink rows={rows} nr={nr} K={K} scale={scale} pad={pad} ws={ws}", flush=True)
     rng = np.random.default_rng(rows * 31 + nr * 7 + K)
     ldx = K + pad
     x_bits, X = _bf16(rng, (rows, ldx))
@@ -109,7 +113,9 @@ def test_lora_shrink(rows, nr, K, scale, pad):
     ref = scale * (X[:, :K] @ A.T)
     U = torch.zeros((rows, nr), dtype=torch.int16, device="cuda")
     dX, dA = _dev(x_bits), _dev(a_bits)  # held until the kernel has run
-    st = hed.orthrus_lora_shrink_bf16(dX.data_ptr(), ldx, dA.data_ptr(), rows, nr, K, scale, U.data_ptr())
+    W = torch.full((8 * rows * nr,), float("nan"), device="cuda") if ws else None
+    st = hed.orthrus_lora_shrink_bf16(dX.data_ptr(), ldx, dA.data_ptr(), rows, nr, K, scale, U.data_ptr(),
+                                      W.data_ptr() if ws else None, 32 * rows * nr if ws else 0)
     assert st == hed.OK
     torch.cuda.synchronize()
     got = bf16_bits_to_f32(U.cpu().numpy().view(np.uint16)).astype(np.float64)
