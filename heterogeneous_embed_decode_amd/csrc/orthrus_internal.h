@@ -42,7 +42,7 @@ constexpr int ATTN_ROWS = 128;       // (token, head) rows per chunk workgroup
 constexpr int ATTN_WAVES = 4;
 constexpr int DEC_SPLIT_VEC = 128;   // keys per decode workgroup, head dims 16 and 32 (32 per wave)
 constexpr int DEC_SPLIT_MIN = 128;   // keys per decode workgroup, head dims 64 and 128: 128 ..
-constexpr int DEC_SPLIT_MAX = 512;   // .. 512, the largest that still gives enough workgroups
+constexpr int DEC_SPLIT_MAX = 4096;  // .. 4096, the largest that still gives enough workgroups
 constexpr int DEC_MIN_WGS = 2048;    // decode workgroups wanted before a larger split is taken
 
 // keys per decode workgroup the decode path accepts for a head dim

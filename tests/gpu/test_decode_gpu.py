@@ -1,6 +1,7 @@
 """Decode attention through orthrus_step against the oracle: decode-heavy
-batches whose sizes select each decode split length (512, 256 and 128 keys
-per workgroup), every grouped-query ratio at head dims 64 and 128, page
+batches whose sizes select each decode split length (4096 down to 128 keys
+per workgroup; at 4096 every row of these batches is one split, with no
+combine), every grouped-query ratio at head dims 64 and 128, page
 sizes that do and do not divide the 16-key blocks (5, 7, 16, 32, 64, 128),
 and contexts on block and split boundaries.  Weights are drawn wider than the model default
 (std 0.05) so that attention is far from uniform and its output is not
@@ -41,9 +42,9 @@ def pages_needed(cfg, ctxs, extra_chunks=()):
 
 
 def expected_split(cfg, ctxs):
-    """The split the library picks: the largest of 512/256/128 keys that
-    still gives 2048 decode workgroups."""
-    split = 512 if cfg.head_dim >= 64 else 128
+    """The split the library picks: the largest of 4096, 2048, ..., 128 keys
+    that still gives 2048 decode workgroups."""
+    split = 4096 if cfg.head_dim >= 64 else 128
     while split > 128 and cfg.n_kv_heads * sum((int(c) + split) // split for c in ctxs) < 2048:
         split //= 2
     return split
@@ -51,7 +52,7 @@ def expected_split(cfg, ctxs):
 
 CASES = [
     # (name, cfg, contexts, embedding chunks)
-    ("hd128-g4-ps16-split512",
+    ("hd128-g4-ps16-split1024",
      sm.ModelConfig(n_layers=1, d_model=512, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn_dim=512,
                     vocab=512, page_size=16, rope_theta=1e6),
      [0, 1, 15, 16, 17, 63, 64, 65, 511, 512, 513, 1023] + list(np.random.default_rng(1).integers(1000, 3000, 130)),
@@ -61,7 +62,7 @@ CASES = [
                     vocab=300, page_size=16, rope_theta=1e6),
      list(np.random.default_rng(2).integers(300, 1500, 200)) + [127, 128, 129],
      []),
-    ("hd64-g1-ps7-split512",
+    ("hd64-g1-ps7-split1024",
      sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=8, head_dim=64, ffn_dim=256,
                     vocab=300, page_size=7, rope_theta=1e4),
      list(np.random.default_rng(3).integers(500, 2500, 170)) + [6, 7, 8, 14, 15],
@@ -89,6 +90,23 @@ CASES = [
                     vocab=300, page_size=64, rope_theta=1e6),
      list(np.random.default_rng(7).integers(300, 1200, 100)) + [63, 64, 65, 127, 128],
      [(200, 0), (130, 64), (77, 300)]),
+    # one workgroup per row and KV head (the boundary contexts 4095 and 4096
+    # give one split and two), two splits of 2048 per row, and 512
+    ("hd64-g1-ps16-split4096",
+     sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=8, head_dim=64, ffn_dim=256,
+                    vocab=300, page_size=16, rope_theta=1e6),
+     list(np.random.default_rng(9).integers(300, 1800, 254)) + [4095, 4096],
+     [(50, 0)]),
+    ("hd64-g2-ps32-split2048",
+     sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=4, head_dim=64, ffn_dim=256,
+                    vocab=300, page_size=32, rope_theta=1e6),
+     list(np.random.default_rng(10).integers(2100, 3900, 300)),
+     []),
+    ("hd128-g4-ps16-split512",
+     sm.ModelConfig(n_layers=1, d_model=512, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn_dim=512,
+                    vocab=512, page_size=16, rope_theta=1e6),
+     list(np.random.default_rng(11).integers(1000, 3000, 62)) + [511, 512, 513],
+     []),
     ("hd64-g2-ps128-split256",
      sm.ModelConfig(n_layers=1, d_model=256, n_q_heads=8, n_kv_heads=4, head_dim=64, ffn_dim=256,
                     vocab=300, page_size=128, rope_theta=1e4),

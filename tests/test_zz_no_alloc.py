@@ -90,19 +90,20 @@ def test_noalloc_matches_step_two_calls():
 
 
 def test_noalloc_refuses_partials_beyond_scratch():
-    """600 decode rows at context 3500 need 600 x 8 x 7 partial results of
-    4 x 130 fp32 values (70 MB), beyond the 60 MiB partial area: ECAPACITY,
-    nothing launched.  The rows share their first 218 pages (read only) and
-    each has its own last page, where its new token would go."""
-    cfg = sm.MISTRAL_7B.with_(n_layers=1)
-    ps, shared, n_dec = cfg.page_size, 218, 600
+    """200 decode rows at context 100000 (pages of 128 keys) take splits of
+    4096 keys, 25 per row: 200 x 8 x 25 partial results of 4 x 130 fp32
+    values (83 MB), beyond the 60 MiB partial area: ECAPACITY, nothing
+    launched.  The rows share their first 781 pages (read only) and each
+    has its own last page, where its new token would go."""
+    cfg = sm.MISTRAL_7B.with_(n_layers=1, page_size=128)
+    ps, shared, n_dec, ctx = cfg.page_size, 781, 200, 100000
     n_pages = shared + n_dec
-    assert shared * ps <= 3500 < (shared + 1) * ps
+    assert shared * ps <= ctx < (shared + 1) * ps
     bits = sm.make_weights(cfg, seed=0)
     dev = DeviceModel(cfg, bits, n_pages, max_tokens=1024, max_items=1024, max_pool_slots=4)
     items, pages = [], []
     for i in range(n_dec):
-        items.append(wl.Item(kind=wl.DECODE, req_id=i, n_tokens=1, ctx_len=3500, page_off=len(pages),
+        items.append(wl.Item(kind=wl.DECODE, req_id=i, n_tokens=1, ctx_len=ctx, page_off=len(pages),
                              n_pages=shared + 1))
         pages.extend(range(shared))
         pages.append(shared + i)
