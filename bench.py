@@ -113,7 +113,9 @@ def step_roofline_ms(cfg, batch, meta):
         terms["rope_table"] = t(*w["rope_table"])
     else:
         terms["rope_kv"] = L * t(0.0, 2.0 * T * (cfg.q_dim + cfg.kv_dim) * 2 + 2.0 * T * 2 * cfg.kv_dim)
-    terms["final_norm"] = t(0.0, T * d * 4.0 + (meta["n_embed_rows"] + meta["n_logits"]) * d * 4.0)
+    # the final norm reads the embedding and logit rows of the residual and
+    # writes the logit rows (bf16) and one 1/rms per embedding row
+    terms["final_norm"] = t(0.0, (meta["n_embed_rows"] + meta["n_logits"]) * d * 4.0 + meta["n_logits"] * d * 2.0)
     terms["lm_head"] = t(*w["lm_head"])
     terms["pool"] = t(*w["pool"])
     return 1e3 * sum(terms.values()), {k: round(1e3 * v, 4) for k, v in terms.items()}
@@ -167,7 +169,8 @@ def chunk_only(batch):
 
 def pool_bytes(cfg, batch):
     """HBM bytes of the pooling kernels per step: streaming heads read the
-    chunk's fp32 rows once; the buffered head also writes them to the
+    chunk's fp32 residual rows once (and one 1/rms per row, not counted);
+    the buffered head also writes them to the
     slot's buffer and, on the last chunk, reads the rows buffered by earlier
     chunks; kept heads touch one row; every head reads and writes its
     d-vector state and the emitted row (read again when the L2 flag

@@ -23,7 +23,8 @@ struct orthrus_engine {
   // workspace
   float *x = nullptr;
   uint16_t *h = nullptr, *qkv = nullptr, *o = nullptr, *act = nullptr, *U = nullptr;
-  float *hf = nullptr;
+  float *hf = nullptr;  // fp32 models: the normalised embedding rows
+  float *rs = nullptr;  // bf16 models: 1/rms of the embedding rows
   uint16_t *hl = nullptr;
   double *inv_freq = nullptr;
   float *rope_cs = nullptr;  // [T][head_dim] cos/sin table of the step (bf16 models)
@@ -180,7 +181,7 @@ static void free_all(orthrus_engine *e) {
   e->marks.clear();
   for (auto ev : e->ev_free) (void)hipEventDestroy(ev);
   e->ev_free.clear();
-  void *ptrs[] = {e->x, e->h, e->qkv, e->o, e->act, e->U, e->hf, e->hl, e->inv_freq,
+  void *ptrs[] = {e->x, e->h, e->qkv, e->o, e->act, e->U, e->hf, e->rs, e->hl, e->inv_freq,
                   e->rope_cs, e->lora_ws, e->part_ml, e->part_o, e->meta_dev};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
@@ -254,7 +255,8 @@ orthrus_status orthrus_create(const orthrus_model_cfg *cfg, const orthrus_weight
       {(void **)&eng->o, T * qd * es},
       {(void **)&eng->act, T * (size_t)c.ffn_dim * es},
       {(void **)&eng->U, T * (size_t)std::max(3 * c.lora_rank, 8) * es},
-      {(void **)&eng->hf, T * d * 4},
+      {(void **)&eng->hf, c.dtype == ORTHRUS_F32 ? T * d * 4 : 4},
+      {(void **)&eng->rs, T * 4},
       {(void **)&eng->hl, T * d * es},
       {(void **)&eng->inv_freq, (size_t)hd / 2 * 8},
       {(void **)&eng->rope_cs, T * hd * 4},
@@ -632,7 +634,7 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
     HIPCHK(hipMemcpyAsync(hidden_out, eng->x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s), "hidden copy");
   LCHK(launch_final_norm(eng->x, (const uint16_t *)eng->w.g_final, d_logit,
                          norm_subset ? meta_dev + o_norm : nullptr,
-                         norm_subset ? (int)norm_rows.size() : TE, G, eng->hf, eng->hl, d, c.rms_eps, s),
+                         norm_subset ? (int)norm_rows.size() : TE, G, eng->rs, eng->hl, d, c.rms_eps, s),
        "final_norm");
   if (G > 0)
     LCHK(launch_gemm(eng->hl, d, (const uint16_t *)eng->w.lm_head, d, logits, c.vocab, G, c.vocab, d, EPI_F32,
@@ -642,8 +644,12 @@ static orthrus_status step_impl(orthrus_engine *eng, const orthrus_batch *batch,
   if (n_segs) {
     bool any_l2 = false;  // an emitted embedding is scaled to unit length
     for (size_t q = 0; q < n_segs; ++q) any_l2 |= (p.pool_segs[q * 8 + 3] & ORTHRUS_POOL_L2) && p.pool_segs[q * 8 + 5];
-    LCHK(launch_pool(eng->hf, d_segs, (int)n_segs, pool->sum, pool->wsum, pool->kept, pool->buf,
-                     pool->buf_rows, emb, d, any_l2, s), "pool");
+    // bf16 models pool the residual rows through the final norm's 1/rms;
+    // fp32 models pool the rows their final norm wrote
+    const bool f32 = c.dtype == ORTHRUS_F32;
+    LCHK(launch_pool(f32 ? eng->hf : eng->x, f32 ? nullptr : eng->rs, (const uint16_t *)eng->w.g_final, d_segs,
+                     (int)n_segs, pool->sum, pool->wsum, pool->kept, pool->buf, pool->buf_rows, emb, d, any_l2, s),
+         "pool");
   }
   HIPCHK(hipEventRecord(eng->done, s), "hipEventRecord");
   eng->last_stream = s;

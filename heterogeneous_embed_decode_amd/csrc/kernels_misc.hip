@@ -157,13 +157,15 @@ __global__ __launch_bounds__(64) void rope_table_kernel(const int32_t *pos, cons
   }
 }
 
-// Final RMSNorm for the rows the outputs need: blocks [0, n_embed) normalise
-// embedding rows (emb_rows[b], or row b when emb_rows is null) into hf at
-// their row (fp32, pooler input); blocks [n_embed, n_embed + n_logit)
-// normalise logit_rows[] into hl (bf16, LM-head input).
+// Final RMSNorm for the rows the outputs need: blocks [0, n_embed) take the
+// 1/rms of embedding rows (emb_rows[b], or row b when emb_rows is null) into
+// rs at their row, which the pooler applies to the residual rows as it
+// reads them (no normalised copy of the rows is written); blocks
+// [n_embed, n_embed + n_logit) normalise logit_rows[] into hl (bf16,
+// LM-head input).
 __global__ __launch_bounds__(256) void final_norm_kernel(const float *x, const uint16_t *g,
                                                          const int32_t *logit_rows, const int32_t *emb_rows,
-                                                         int n_embed, float *hf, uint16_t *hl, int d, float eps) {
+                                                         int n_embed, float *rs, uint16_t *hl, int d, float eps) {
   __shared__ float red[4];
   const int b = blockIdx.x;
   const bool emb = b < n_embed;
@@ -185,15 +187,7 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float *x, const u
     norm_write_bf16(v, g, hl + (size_t)(b - n_embed) * d, nv4, inv);
     return;
   }
-#pragma unroll
-  for (int j = 0; j < NORM_MAXV; ++j) {
-    const int c = threadIdx.x + j * 256;
-    if (c >= nv4) break;
-    const uint2 gw = *(const uint2 *)(g + c * 4);
-    *(float4 *)(hf + (size_t)row * d + c * 4) =
-        make_float4(v[j].x * inv * lo_bf(gw.x), v[j].y * inv * hi_bf(gw.x), v[j].z * inv * lo_bf(gw.y),
-                    v[j].w * inv * hi_bf(gw.y));
-  }
+  if (threadIdx.x == 0) rs[row] = inv;
 }
 
 // Segmented pooling.  Segment s = (row0, n, slot, kind, first, last, ctx,
@@ -204,9 +198,17 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float *x, const u
 // afterwards so no block reads a value another block has already advanced.
 // d is a multiple of 8, so a column group never straddles the row end
 // except as a whole.
-__global__ __launch_bounds__(256) void pool_kernel(const float *hf, const int32_t *segs, float *sum,
-                                                   const float *wsum, float *kept, float *buf, int buf_rows,
-                                                   float *emb, int d) {
+// The pooled hidden state is the final norm's output (Efficient Iterative
+// Retrieval with Heterogeneous Batching, §3.2: the output kernels work on
+// the contiguous slice of their item type, with no gather or intermediate
+// copy).  SCALED: the pooler reads the item's slice of the residual stream
+// and applies the final norm there, (x rs[row]) g[col], the same products
+// in the same order as the norm itself; otherwise src rows are already
+// normalised (the fp32 path).
+template <bool SCALED>
+__global__ __launch_bounds__(256) void pool_kernel(const float *src, const float *rs, const uint16_t *g,
+                                                   const int32_t *segs, float *sum, const float *wsum, float *kept,
+                                                   float *buf, int buf_rows, float *emb, int d) {
   __shared__ float4 part[4][64];
   const int32_t *sg = segs + blockIdx.x * 8;
   const int row0 = sg[0], n = sg[1], slot = sg[2], kind = sg[3] & ~ORTHRUS_POOL_L2;
@@ -214,6 +216,18 @@ __global__ __launch_bounds__(256) void pool_kernel(const float *hf, const int32_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = blockIdx.y * 256 + lane * 4;  // first of this lane's 4 columns
   const bool cols = j < d;
+  float gc[4] = {1.f, 1.f, 1.f, 1.f};
+  if (SCALED && cols) {
+    const uint2 gw = *(const uint2 *)(g + j);
+    gc[0] = lo_bf(gw.x); gc[1] = hi_bf(gw.x); gc[2] = lo_bf(gw.y); gc[3] = hi_bf(gw.y);
+  }
+  // the final norm's output at row row0 + r, this lane's 4 columns
+  auto rowv = [&](int r) -> float4 {
+    const float4 v = *(const float4 *)(src + (size_t)(row0 + r) * d + j);
+    if (!SCALED) return v;
+    const float inv = rs[row0 + r];
+    return make_float4(v.x * inv * gc[0], v.y * inv * gc[1], v.z * inv * gc[2], v.w * inv * gc[3]);
+  };
   if (kind == ORTHRUS_POOL_BUFFER) {
     // Keep this chunk's rows at their positions; on the last chunk run the
     // head over all N rows.  Wave w owns the positions p = w (mod 4) and
@@ -221,7 +235,6 @@ __global__ __launch_bounds__(256) void pool_kernel(const float *hf, const int32_
     // chunk's rows as it copies them; the waves meet in a fixed order, so
     // the summation order depends on N alone.
     float *bs = buf + (size_t)slot * buf_rows * d + j;
-    const float *hs = hf + (size_t)row0 * d + j;
     float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (cols) {
       if (last) {
@@ -237,7 +250,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const float *hf, const int32_
       const int p0 = ctx + ((wave - ctx) & 3);   // first position >= ctx with p = wave (mod 4)
 #pragma unroll 4
       for (int p = p0; p < ctx + n; p += 4) {
-        const float4 v = *(const float4 *)(hs + (size_t)(p - ctx) * d);
+        const float4 v = rowv(p - ctx);
         *(float4 *)(bs + (size_t)p * d) = v;
         s4.x += v.x;
         s4.y += v.y;
@@ -262,10 +275,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const float *hf, const int32_
   if (kind == ORTHRUS_POOL_MEAN || kind == ORTHRUS_POOL_WMEAN) {
     float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (cols) {
-      const float *col = hf + (size_t)row0 * d + j;
 #pragma unroll 4
       for (int r = wave; r < n; r += 4) {
-        const float4 v = *(const float4 *)(col + (size_t)r * d);
+        const float4 v = rowv(r);
         const float wgt = kind == ORTHRUS_POOL_MEAN ? 1.f : (float)(ctx + r + 1);
         s4.x += wgt * v.x;
         s4.y += wgt * v.y;
@@ -291,16 +303,14 @@ __global__ __launch_bounds__(256) void pool_kernel(const float *hf, const int32_
   } else {
     if (wave != 0 || !cols) return;
     float *k = kept + (size_t)slot * d + j;
-    const float *src = hf + (size_t)row0 * d + j;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (kind == ORTHRUS_POOL_CLS) {
-        if (first) k[q] = src[q];
-      } else {
-        k[q] = src[(size_t)(n - 1) * d + q];
-      }
-      if (last) emb[(size_t)out * d + j + q] = k[q];
+    const bool take = kind != ORTHRUS_POOL_CLS || first;
+    if (take) {
+      const float4 v = rowv(kind == ORTHRUS_POOL_CLS ? 0 : n - 1);
+      k[0] = v.x; k[1] = v.y; k[2] = v.z; k[3] = v.w;
     }
+    if (last)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) emb[(size_t)out * d + j + q] = k[q];
   }
 }
 
@@ -375,19 +385,24 @@ int launch_rope_kv(uint16_t *qkv, const int32_t *pos, const int32_t *slot, const
 }
 
 int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_rows, const int32_t *emb_rows,
-                      int n_embed, int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream) {
+                      int n_embed, int n_logit, float *rs, uint16_t *hl, int d, float eps, void *stream) {
   if (n_embed + n_logit <= 0) return 0;
   hipLaunchKernelGGL(final_norm_kernel, dim3(n_embed + n_logit), dim3(256), 0, (hipStream_t)stream, x,
-                     g, logit_rows, emb_rows, n_embed, hf, hl, d, eps);
+                     g, logit_rows, emb_rows, n_embed, rs, hl, d, eps);
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }
 
-int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, float *wsum, float *kept, float *buf,
-                int buf_rows, float *emb, int d, bool any_l2, void *stream) {
+int launch_pool(const float *src, const float *rs, const uint16_t *g, const int32_t *segs, int n_segs, float *sum,
+                float *wsum, float *kept, float *buf, int buf_rows, float *emb, int d, bool any_l2, void *stream) {
   if (n_segs <= 0) return 0;
-  hipLaunchKernelGGL(pool_kernel, dim3(n_segs, (d + 255) / 256), dim3(256), 0, (hipStream_t)stream, hf,
-                     segs, sum, wsum, kept, buf, buf_rows, emb, d);
+  const dim3 grid(n_segs, (d + 255) / 256);
+  if (rs)
+    hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream, src, rs, g, segs, sum, wsum,
+                       kept, buf, buf_rows, emb, d);
+  else
+    hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(256), 0, (hipStream_t)stream, src, rs, g, segs, sum, wsum,
+                       kept, buf, buf_rows, emb, d);
   ORTHRUS_LAUNCH_CHECK();
   hipLaunchKernelGGL(pool_wsum_kernel, dim3((n_segs + 63) / 64), dim3(64), 0, (hipStream_t)stream, segs,
                      n_segs, wsum);

@@ -114,8 +114,9 @@ int launch_attn_ragged(const uint16_t *qkv, int ld_qkv, const uint16_t *kc, cons
 int launch_attn_combine(const DevItem *items, const int32_t *dec_items, int n_dec,
                         const float *part_ml, const float *part_o, uint16_t *o, int ld_o,
                         int Hq, int Hkv, int hd, void *stream);
+// embedding rows: their 1/rms into rs[row]; logit rows: normalised into hl
 int launch_final_norm(const float *x, const uint16_t *g, const int32_t *logit_rows, const int32_t *emb_rows,
-                      int n_embed, int n_logit, float *hf, uint16_t *hl, int d, float eps, void *stream);
+                      int n_embed, int n_logit, float *rs, uint16_t *hl, int d, float eps, void *stream);
 // fp32 path (kernels_f32.hip)
 int launch_gemm_f32(const float *A, int lda, const float *B, int ldb, float *C, int ldc, int M, int N, int K,
                     int epi, int b_up_row, float alpha, const float *U, int ldu, const float *Bx, int r, int lrows,
@@ -143,7 +144,9 @@ int launch_lora_shrink(const uint16_t *X, int ldx, const uint16_t *A, int rows, 
 int launch_sample(const float *logits, int64_t ld, int n_rows, int V, const float *temperature,
                   const float *top_p, const uint32_t *uniforms, int32_t *tokens, void *stream);
 int launch_hash_fill(uint16_t *dst, uint64_t n, uint32_t seed, uint32_t tensor_id, uint64_t start, void *stream);
-int launch_pool(const float *hf, const int32_t *segs, int n_segs, float *sum, float *wsum, float *kept, float *buf,
-                int buf_rows, float *emb, int d, bool any_l2, void *stream);
+// rs non-null: src is the residual stream and row r pools (src[r] rs[r]) g;
+// rs null: src rows are already normalised
+int launch_pool(const float *src, const float *rs, const uint16_t *g, const int32_t *segs, int n_segs, float *sum,
+                float *wsum, float *kept, float *buf, int buf_rows, float *emb, int d, bool any_l2, void *stream);
 
 }  // namespace orthrus
