@@ -19,10 +19,11 @@
 //     which the running nucleus weight exceeds x.
 // tau comes from a most-significant-digit-first radix select whose bins
 // hold weight sums (digits of 8, 8, 8 and 7 bits from bit 30 down).  The
-// weights are recomputed from the logits on every pass over the row (six
-// passes of 4V bytes, the later ones from L2), so the kernel needs no memory
-// beyond its inputs and outputs.  At a few hundred rows the kernel is bound
-// by load latency and workgroup barriers rather than by HBM bandwidth.
+// first radix pass forms the weights from the logits; when the row's
+// weights fit in LDS (vocabularies up to 38400 tokens: 150 KB) they are kept
+// there and the later radix passes and the draw read them back, otherwise
+// every pass recomputes them from the logits (the later reads from L2).
+// Either way the kernel needs no memory beyond its inputs and outputs.
 #include "device_common.h"
 #include "orthrus_internal.h"
 
@@ -106,6 +107,7 @@ __device__ __forceinline__ uint64_t draw_point(uint64_t mass, uint64_t U) {
 constexpr int SMP_T = 1024;
 constexpr int SMP_W = SMP_T / 64;
 constexpr int SMP_U = 4;
+constexpr int SMP_CACHE_GROUPS = 9600;  // groups of 4 weights kept in LDS (150 KB)
 
 __device__ __forceinline__ float4 load4(const float *L, int g, int V, int vec_ok) {
   const int i = 4 * g;
@@ -118,11 +120,13 @@ __device__ __forceinline__ float4 load4(const float *L, int g, int V, int vec_ok
   return r;
 }
 
+// cached: the launch gave 16 n_grp bytes of dynamic LDS for the weights
 __global__ __launch_bounds__(SMP_T) void sample_kernel(const float *__restrict__ logits, int64_t ld, int V,
                                                        int vec_ok, const float *__restrict__ temp,
                                                        const float *__restrict__ top_p,
                                                        const uint32_t *__restrict__ uni,
-                                                       int32_t *__restrict__ out) {
+                                                       int32_t *__restrict__ out, int cached) {
+  extern __shared__ uint4 qcache[];  // weights of group g (tokens 4g .. 4g+3), zero past V
   __shared__ unsigned long long hist[2][256];
   __shared__ unsigned long long seg_a[SMP_W];
   __shared__ uint32_t seg_c[SMP_W];
@@ -195,16 +199,33 @@ __global__ __launch_bounds__(SMP_T) void sample_kernel(const float *__restrict__
     uint64_t h0 = 0;                                // digit 0 is summed in registers
 #pragma unroll 1
     for (int g0 = tid; g0 < n_grp; g0 += SMP_U * SMP_T) {
-      float4 v[SMP_U];
+      uint32_t qq[SMP_U][4];
+      if (cached && lev > 0) {
 #pragma unroll
-      for (int u = 0; u < SMP_U; ++u) v[u] = load4(L, g0 + u * SMP_T, V, vec_ok);
+        for (int u = 0; u < SMP_U; ++u) {
+          const int gi = g0 + u * SMP_T;
+          const uint4 w4 = gi < n_grp ? qcache[gi] : make_uint4(0u, 0u, 0u, 0u);
+          qq[u][0] = w4.x; qq[u][1] = w4.y; qq[u][2] = w4.z; qq[u][3] = w4.w;
+        }
+      } else {
+        float4 v[SMP_U];
+#pragma unroll
+        for (int u = 0; u < SMP_U; ++u) v[u] = load4(L, g0 + u * SMP_T, V, vec_ok);
+#pragma unroll
+        for (int u = 0; u < SMP_U; ++u) {
+          const int i = 4 * (g0 + u * SMP_T);
+          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) qq[u][c] = i + c < V ? weight_of(e[c], mx, s) : 0u;
+          if (cached && g0 + u * SMP_T < n_grp)
+            qcache[g0 + u * SMP_T] = make_uint4(qq[u][0], qq[u][1], qq[u][2], qq[u][3]);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < SMP_U; ++u) {
-        const int i = 4 * (g0 + u * SMP_T);
-        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t q = i + c < V ? weight_of(e[c], mx, s) : 0u;
+          const uint32_t q = qq[u][c];
           const uint32_t dg = (q >> sh) & mask;
           if ((q >> hs) == pref) {
             if (dg == 0) h0 += q;
@@ -257,22 +278,31 @@ __global__ __launch_bounds__(SMP_T) void sample_kernel(const float *__restrict__
   const int cb = w * cpw, ce = min(n_chunk, cb + cpw);
   uint64_t sa = 0;
   uint32_t sc = 0;
+  // the weights of group g (tokens 4g .. 4g+3; zero past V or for a chunk
+  // past the wave's segment)
+  auto group_q = [&](int gi, bool ok, uint32_t *q) {
+    if (cached) {
+      const uint4 w4 = ok && gi < n_grp ? qcache[gi] : make_uint4(0u, 0u, 0u, 0u);
+      q[0] = w4.x; q[1] = w4.y; q[2] = w4.z; q[3] = w4.w;
+      return;
+    }
+    const float4 v = load4(L, ok ? gi : n_grp, V, vec_ok);
+    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q[c] = (ok && 4 * gi + c < V) ? weight_of(e[c], mx, s) : 0u;
+  };
 #pragma unroll 1
   for (int c0 = cb; c0 < ce; c0 += SMP_U) {
-    float4 v[SMP_U];
+    uint32_t qq[SMP_U][4];
 #pragma unroll
-    for (int u = 0; u < SMP_U; ++u) v[u] = load4(L, c0 + u < ce ? (c0 + u) * 64 + lane : n_grp, V, vec_ok);
+    for (int u = 0; u < SMP_U; ++u) group_q((c0 + u) * 64 + lane, c0 + u < ce, qq[u]);
 #pragma unroll
-    for (int u = 0; u < SMP_U; ++u) {
-      const int i = 4 * ((c0 + u) * 64 + lane);
-      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    for (int u = 0; u < SMP_U; ++u)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t q = (c0 + u < ce && i + c < V) ? weight_of(e[c], mx, s) : 0u;
-        sa += q > tau ? q : 0u;
-        sc += q == tau;
+        sa += qq[u][c] > tau ? qq[u][c] : 0u;
+        sc += qq[u][c] == tau;
       }
-    }
   }
   sa = wave_sum_u64(sa);
 #pragma unroll
@@ -293,15 +323,12 @@ __global__ __launch_bounds__(SMP_T) void sample_kernel(const float *__restrict__
   constexpr uint64_t M40 = (1ull << 40) - 1;
 #pragma unroll 1
   for (int ch = cb; ch < ce; ++ch) {
-    const int i = 4 * (ch * 64 + lane);
-    const float4 v = load4(L, ch * 64 + lane, V, vec_ok);
-    const float e[4] = {v.x, v.y, v.z, v.w};
     uint32_t qv[4];
+    group_q(ch * 64 + lane, true, qv);
     uint64_t la = 0;
     uint32_t lc = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      qv[c] = i + c < V ? weight_of(e[c], mx, s) : 0u;
       la += qv[c] > tau ? qv[c] : 0u;
       lc += qv[c] == tau;
     }
@@ -338,8 +365,18 @@ __global__ __launch_bounds__(SMP_T) void sample_kernel(const float *__restrict__
 int launch_sample(const float *logits, int64_t ld, int n_rows, int V, const float *temperature,
                   const float *top_p, const uint32_t *uniforms, int32_t *tokens, void *stream) {
   const int vec_ok = (ld % 4 == 0) && (((uintptr_t)logits & 15) == 0);
-  hipLaunchKernelGGL(sample_kernel, dim3(n_rows), dim3(SMP_T), 0, (hipStream_t)stream, logits, ld, V, vec_ok,
-                     temperature, top_p, uniforms, tokens);
+  const int n_grp = (V + 3) / 4;
+  const int cached = n_grp <= SMP_CACHE_GROUPS && temperature != nullptr;
+  const size_t lds = cached ? (size_t)n_grp * 16 : 0;
+  static bool attr_set = false;  // per process
+  if (cached && !attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void *)sample_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             SMP_CACHE_GROUPS * 16);
+    if (e != hipSuccess) return (int)e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(sample_kernel, dim3(n_rows), dim3(SMP_T), lds, (hipStream_t)stream, logits, ld, V, vec_ok,
+                     temperature, top_p, uniforms, tokens, cached);
   ORTHRUS_LAUNCH_CHECK();
   return 0;
 }

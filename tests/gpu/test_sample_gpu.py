@@ -46,8 +46,10 @@ def _case(rng, n, V, temps, tops, scale=3.0, quant=None):
 
 
 @pytest.mark.parametrize("n,V,seed", [(1, 1, 0), (7, 37, 1), (16, 2047, 2), (16, 2049, 3), (9, 5000, 4),
-                                        (12, 4097, 6), (3, 128256, 5)])
+                                        (12, 4097, 6), (3, 128256, 5), (4, 38400, 7), (4, 38401, 8)])
 def test_sampler_matches_oracle(n, V, seed):
+    """Vocabularies up to 38400 tokens keep the row's weights in LDS after
+    the first radix pass; 38401 and 128256 recompute them on every pass."""
     rng = np.random.default_rng(seed)
     print(f"[sample n={n} V={V} seed={seed}]", flush=True)
     L, temp, top, uni = _case(rng, n, V, [0.0, 0.25, 0.7, 1.0, 1.6], [0.05, 0.5, 0.9, 0.99, 1.0])
