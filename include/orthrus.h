@@ -223,7 +223,8 @@ orthrus_status orthrus_step(orthrus_engine *eng, const orthrus_batch *batch,
  * and 12 per attention work entry: one per 128/(Hq/Hkv) rows of a chunk
  * per KV head, one per decode split per KV head) and 60 MiB of decode
  * partial results ((Hq/Hkv) * (2 + head_dim) * 4 bytes per decode split
- * per KV head; decode rows split their keys in pieces of 128 to 512);
+ * per KV head; decode rows split their keys in pieces of 128 to 4096, the
+ * largest that still gives 2048 decode workgroups);
  * beyond either, ECAPACITY before any device work, with the limit in
  * orthrus_last_error.  Every call on one device shares that device's
  * array: calls that overlap on one device (two engines on two streams,
