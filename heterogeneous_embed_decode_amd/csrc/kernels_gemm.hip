@@ -438,7 +438,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
   // rows' cos/sin and KV slots are loaded before the LDS exchange that
   // precedes their use, so their latency overlaps it.
   auto qkv_epilogue = [&]() {
-    static_assert(EPI != EPI_QKV || (BM == 256 && BN == 256 && WM == 2 && WN == 4),
+    static_assert(EPI != EPI_QKV || (BM == 256 && BN == 256 && WM == 2 && WN == 4 && MT == 32),
                   "the QKV epilogue assumes 256x256 tiles on 2x4 waves");
     constexpr int RP = NT / 16;   // rows covered by one pass of all threads
     constexpr int NR = 128 / RP;  // rows per thread per half tile
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g) {
           for (int j = 0; j < NI; ++j)
 #pragma unroll
             for (int e = 0; e < NE; ++e) {
-              const int row = i * MT + (MT == 32 ? (e / 4) * 8 + (lane >> 5) * 4 + (e % 4) : (lane >> 4) * 4 + e);
+              const int row = i * MT + (e / 4) * 8 + (lane >> 5) * 4 + (e % 4);
               const int col = wn * WCN + j * MT + jc;
               xs[row * 256 + (col ^ (((row >> 2) & 1) << 5))] = g.alpha * acc[i][j][e];
             }
