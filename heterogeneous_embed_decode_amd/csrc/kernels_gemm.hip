@@ -656,7 +656,7 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
       if (big) {
         const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
         const int rem = tiles % gemm_cu_count();
-        return launch_cfg<256, 256, 4, 2, 64, 2, EPI_RESID>(a, s, rem != 0 && rem < gemm_cu_count() / 2 ? gemm_cu_count() : 0);
+        return launch_cfg<256, 256, 2, 4, 64, 2, EPI_RESID>(a, s, rem != 0 && rem < gemm_cu_count() / 2 ? gemm_cu_count() : 0);
       }
       if (skinny) return launch_cfg<64, 128, 2, 2, 64, 4, EPI_RESID>(a, s);
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);
