@@ -25,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-SOURCES = ["pack.cpp", "engine.cpp", "sched.cpp", "kernels_gemm.hip", "kernels_attn.hip", "kernels_misc.hip",
+SOURCES = ["pack.cpp", "engine.cpp", "sched.cpp", "kernels_gemm.hip", "kernels_gemm_w4.hip", "kernels_attn.hip", "kernels_misc.hip",
            "kernels_sample.hip", "scratch.hip", "kernels_f32.hip"]
 
 

@@ -633,8 +633,11 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
   // weights stream from HBM; 128x128 on 4 waves otherwise.
   const bool big = M >= 512 && N >= 1024;
   const bool skinny = M <= 64;
+  const bool no_adapter = a.U == nullptr;
   switch (epi) {
     case EPI_BF16:
+      if (big && no_adapter && gemm_w4_eligible(lda, ldb, M, N, K, EPI_BF16, 0))
+        return launch_gemm_w4(A, lda, B, ldb, C, ldc, M, N, K, EPI_BF16, 0, alpha, stream);
       if (big) return launch_cfg<256, 256, 2, 4, 64, 2, EPI_BF16>(a, s);
       // few output columns (the adapter shrink, N = 3 x rank): small tiles
       // so that more workgroups share the long K loop
@@ -662,6 +665,12 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
       return launch_cfg<128, 128, 2, 2, 64, 2, EPI_RESID>(a, s);
     case EPI_SWIGLU:
       if (big) {
+        // 256-row tiles on the one-wave-per-SIMD kernel where it applies
+        auto rows256 = [&](const GemmArgs &x) {
+          if (gemm_w4_eligible(lda, ldb, x.M, N, K, EPI_SWIGLU, b_up_row))
+            return launch_gemm_w4(x.A, lda, B, ldb, x.C, ldc, x.M, N, K, EPI_SWIGLU, b_up_row, 1.f, stream);
+          return launch_cfg<256, 128, 2, 4, 64, 2, EPI_SWIGLU>(x, s);
+        };
         // a last tile row of at most 64 rows costs a whole extra round of
         // 256-row tiles when the full tile rows fill whole rounds; those
         // rows then go to a launch of 64-row tiles instead
@@ -671,14 +680,14 @@ int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
             (full * tn + cus - 1) / cus < ((full + 1) * tn + cus - 1) / cus) {
           GemmArgs lo = a;
           lo.M = full * 256;
-          if (int r = launch_cfg<256, 128, 2, 4, 64, 2, EPI_SWIGLU>(lo, s)) return r;
+          if (int r = rows256(lo)) return r;
           GemmArgs hi = a;
           hi.A = A + (size_t)lo.M * lda;
           hi.C = (uint16_t *)C + (size_t)lo.M * ldc;
           hi.M = rest;
           return launch_cfg<64, 64, 2, 2, 64, 4, EPI_SWIGLU>(hi, s);
         }
-        return launch_cfg<256, 128, 2, 4, 64, 2, EPI_SWIGLU>(a, s);
+        return rows256(a);
       }
       if (skinny) return launch_cfg<64, 64, 2, 2, 64, 4, EPI_SWIGLU>(a, s);
       return launch_cfg<128, 64, 2, 2, 64, 2, EPI_SWIGLU>(a, s);

@@ -78,6 +78,13 @@ struct LoraArgs {
 
 enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
 
+// The one-wave-per-SIMD kernel (kernels_gemm_w4.hip): SwiGLU or plain bf16
+// outputs, no adapter, K a multiple of 32, A and B each below 1 GiB, at
+// least 256 rows and columns.
+bool gemm_w4_eligible(int lda, int ldb, int M, int N, int K, int epi, int b_up_row);
+int launch_gemm_w4(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C, int ldc, int M, int N, int K,
+                   int epi, int b_up_row, float alpha, void *stream);
+
 int launch_gemm(const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C, int ldc,
                 int M, int N, int K, int epi, int b_up_row, float alpha,
                 const LoraArgs *lora, void *stream);
