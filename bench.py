@@ -192,9 +192,12 @@ def pool_bytes(cfg, batch):
     return tot
 
 
-def kernel_source_digest(name):
+def kernel_source_digest(names):
+    """First 16 hex digits of the SHA-256 of the named csrc files' contents,
+    concatenated in the order given (names separated by spaces)."""
     h = hashlib.sha256()
-    h.update(open(os.path.join(ROOT, "heterogeneous_embed_decode_amd", "csrc", name), "rb").read())
+    for name in names.split():
+        h.update(open(os.path.join(ROOT, "heterogeneous_embed_decode_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
