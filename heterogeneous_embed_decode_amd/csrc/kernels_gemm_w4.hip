@@ -87,14 +87,16 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(W4Args g) {
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)g.B, (short)0, (int)g.b_bytes, 0x00020000);
   // Load lanes: instruction i of wave w fills LDS rows (4 i + w) * 16 + lane / 4,
   // 16-byte chunk position lane % 4, with logical chunk (lane % 4) ^ swizzle.
-  // A row's chunk swizzle is (row >> 2) & 3, so the 16 rows one 16-lane
-  // group of a fragment read touches fall on 16 distinct bank slots.
+  // A row's chunk swizzle is (row >> 1) & 3.  Measured with
+  // SQ_LDS_BANK_CONFLICT on the fragment reads: (row >> 1) & 3 has no bank
+  // conflicts, while (row >> 2) & 3, row & 3 and (row ^ (row >> 2)) & 3 are
+  // conflicted on half of the LDS-active cycles.
   const int lrow = lane >> 2, pc = lane & 3;
   uint32_t aoff[4], boff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (i * 4 + wave) * 16 + lrow;
-    const int kc = pc ^ ((row >> 2) & 3);
+    const int kc = pc ^ ((row >> 1) & 3);
     const int gr = m0 + row;
     aoff[i] = gr < g.M ? (uint32_t)(((size_t)gr * g.lda + kc * 8) * 2) : W4_OOB_ROW;
     int br, ncol;
@@ -119,8 +121,9 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(W4Args g) {
                                                16, boff[idx - 4] + k2, 0, 0, 0);
   };
   // fragment reads: lane l takes row l % 16 of each 16-row block and the 8
-  // k of logical chunk l / 16, stored at position (l / 16) ^ ((l >> 2) & 3)
-  const int fpos = ((lane >> 4) ^ ((lane >> 2) & 3)) * 8 + (lane & 15) * 32;
+  // k of logical chunk l / 16, stored at position (l / 16) ^ ((l >> 1) & 3)
+  // (blocks start at multiples of 16 rows, so the swizzle is the lane's own)
+  const int fpos = ((lane >> 4) ^ ((lane >> 1) & 3)) * 8 + (lane & 15) * 32;
   const uint16_t *const fa_base = As + wm * 128 * 32 + fpos;
   const uint16_t *const fb_base = Bs + wn * 128 * 32 + fpos;
 
