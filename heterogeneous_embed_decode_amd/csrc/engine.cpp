@@ -157,10 +157,16 @@ void build_attn_work(const orthrus_model_cfg &cfg, const orthrus_batch &b, const
       n_parts += cfg.n_kv_heads * ns;
     }
   }
-  // heaviest chunk tiles first (rows x keys)
+  // heaviest chunk tiles first (rows x keys), and longest decode splits
+  // first: workgroups start in list order, so the shortest ones fill the
+  // last round instead of a long one starting late.  Each entry writes its
+  // own partial slot and the combine reads them in a fixed order, so the
+  // order changes no result.
   std::stable_sort(work.begin(), work.end(), [](const AttnWork &a, const AttnWork &c) {
     return (long)a.qn * a.k1 > (long)c.qn * c.k1;
   });
+  std::stable_sort(dec.begin(), dec.end(),
+                   [](const AttnWork &a, const AttnWork &c) { return a.k1 - a.k0 > c.k1 - c.k0; });
   n_chunk = (int)work.size();
   work.insert(work.end(), dec.begin(), dec.end());
 }
