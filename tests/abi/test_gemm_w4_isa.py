@@ -4,8 +4,9 @@ MFMA writing an accumulator register and another instruction touching it.
 The kernel is written so that no such instruction exists between the first
 MFMA and the fence of nops after the K loop; this test compiles the source
 for gfx950 and checks that in the generated code: for every instantiation,
-one K loop holding all 128 MFMAs (two K-steps of 64) and no other
-instruction naming an AGPR from the first MFMA to the fence."""
+one K loop holding all 128 MFMAs (two K-steps of 64), no other
+instruction naming an AGPR from the first MFMA to the fence, and the
+accumulators' zeroing at least 16 instructions before the first MFMA."""
 
 import os
 import re
@@ -51,6 +52,10 @@ def test_no_accumulator_access_inside_the_mfma_region():
         agpr = [l for i, l in enumerate(code) if mfma[0] <= i < fence and not l.startswith("v_mfma")
                 and re.search(r"\ba\d|\ba\[", l)]
         assert not agpr, (name, agpr[:4])
+        # the zeroing writes of the accumulators lie well before the first
+        # MFMA reads them (the hardware needs a few wait states there)
+        zero = [i for i, l in enumerate(code[:mfma[0]]) if re.search(r"\ba\d|\ba\[", l)]
+        assert zero and mfma[0] - zero[-1] >= 16, (name, mfma[0] - zero[-1] if zero else None)
         heads = [i for i, l in enumerate(body) if "Loop Header" in l]
         assert len(heads) == 1, name
         end = next(i for i in range(heads[0], len(body)) if body[i].startswith("s_cbranch"))
